@@ -1,0 +1,187 @@
+"""Seeded generators for the synthetic MoE-layer workloads.
+
+Recipe (every draw is reproducible from ``seed`` alone):
+
+* Each tensor (and, for expert weights, each expert) draws from its own numpy
+  ``Generator`` seeded by ``SeedSequence(seed, spawn_key=(tensor_id, index))``,
+  so a tensor's values do not depend on which other tensors or how many tokens
+  are drawn, and expert ``e`` has the same weights in every view that holds it.
+* Normals are drawn in float32 and scaled by the standard deviation: x ~ N(0,1);
+  gate weights and W13 ~ N(0, 1/H); W2 ~ N(0, 1/I) with the *full* I, also for
+  the tensor-parallel slices.  bf16 inputs are then rounded to nearest even
+  on the float32 bit pattern and kept as uint16 bit patterns.
+* x is drawn once at (T_max, H); a batch of T tokens is its first T rows, so
+  the routing of the sweep's batches is nested.
+* The skewed workloads add a fixed gate bias b_e = -1.2 ln(rho_e), where rho is
+  1 + a seeded permutation of 0..E-1: the routing prior is then proportional
+  to rho^-1.2 (a Zipf law with s = 1.2), standing in for the concentrated
+  token-expert affinity that the Sem-MoE notes report (profiled activation
+  statistics, Key design 1).  The uniform workloads use b = 0.
+
+Nothing here computes any part of the layer.
+"""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from .configs import LayerConfig
+
+# tensor ids used as the first spawn-key element
+_X, _W_GATE, _RHO, _W13, _W2, _W13_SHARED, _W2_SHARED, _W13_TP, _W2_TP = range(9)
+
+ZIPF_S = 1.2
+
+
+def _rng(seed: int, tensor_id: int, index: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(tensor_id, index)))
+
+
+def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits.
+
+    Inputs must be finite.
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def _normal_block(seed, tensor_id, index, shape, std, dtype):
+    z = _rng(seed, tensor_id, index).standard_normal(shape, dtype=np.float32)
+    z *= np.float32(std)
+    return bf16_bits_from_f32(z) if dtype == "bf16" else z
+
+
+def _stack(seed, tensor_id, indices, shape, std, dtype):
+    """Draw one block per index (in parallel threads) and stack them."""
+    out_dtype = np.uint16 if dtype == "bf16" else np.float32
+    out = np.empty((len(indices),) + tuple(shape), dtype=out_dtype)
+
+    def fill(j):
+        out[j] = _normal_block(seed, tensor_id, indices[j], shape, std, dtype)
+
+    workers = max(1, min(16, os.cpu_count() or 1, len(indices)))
+    if workers == 1:
+        for j in range(len(indices)):
+            fill(j)
+    else:
+        with ThreadPoolExecutor(workers) as pool:
+            list(pool.map(fill, range(len(indices))))
+    return out
+
+
+def gate_bias(cfg: LayerConfig, routing: str, seed: int = 0) -> np.ndarray:
+    if routing == "uniform":
+        return np.zeros(cfg.E, dtype=np.float32)
+    if routing != "zipf":
+        raise ValueError(f"unknown routing variant {routing!r}")
+    rho = 1.0 + _rng(seed, _RHO).permutation(cfg.E).astype(np.float64)
+    return (-ZIPF_S * np.log(rho)).astype(np.float32)
+
+
+def ep_rank_for(cfg: LayerConfig, routing: str, seed: int = 0) -> int:
+    """Which EP rank's share to emulate: rank 0 under uniform routing; under
+    skewed routing the rank whose contiguous experts carry the largest prior
+    mass (the straggler that sets an EP step's time)."""
+    if routing == "uniform" or cfg.view != "ep":
+        return 0
+    prior = np.exp(gate_bias(cfg, routing, seed).astype(np.float64))
+    per_rank = prior.reshape(cfg.P, cfg.E // cfg.P).sum(axis=1)
+    return int(np.argmax(per_rank))
+
+
+def make_x(cfg: LayerConfig, T: int, seed: int = 0, T_draw: int = None) -> np.ndarray:
+    T_draw = max(T, T_draw or cfg.T_max)
+    x = _normal_block(seed, _X, 0, (T_draw, cfg.H), 1.0, cfg.dtype)
+    return np.ascontiguousarray(x[:T])
+
+
+def make_gate(cfg: LayerConfig, seed: int = 0) -> np.ndarray:
+    return _normal_block(seed, _W_GATE, 0, (cfg.E, cfg.H), cfg.H ** -0.5, cfg.dtype)
+
+
+def expert_weights(cfg: LayerConfig, experts, seed: int = 0):
+    """Whole routed experts (ids into 0..E-1): W13 (n, 2I, H), W2 (n, H, I)."""
+    experts = list(experts)
+    w13 = _stack(seed, _W13, experts, (2 * cfg.I, cfg.H), cfg.H ** -0.5, cfg.dtype)
+    w2 = _stack(seed, _W2, experts, (cfg.H, cfg.I), cfg.I ** -0.5, cfg.dtype)
+    return w13, w2
+
+
+def shared_weights(cfg: LayerConfig, seed: int = 0):
+    idx = list(range(cfg.n_shared))
+    w13 = _stack(seed, _W13_SHARED, idx, (2 * cfg.I, cfg.H), cfg.H ** -0.5, cfg.dtype)
+    w2 = _stack(seed, _W2_SHARED, idx, (cfg.H, cfg.I), cfg.I ** -0.5, cfg.dtype)
+    return w13, w2
+
+
+def make_layer_inputs(cfg: LayerConfig, T: int, routing: str = "uniform", seed: int = 0,
+                      rank: int = None) -> dict:
+    """Host arrays for one forward pass of ``cfg`` on T tokens.
+
+    Returns x (T,H), w_gate (E,H), gate_bias (E,) float32, w13 (n_groups,2I',H),
+    w2 (n_groups,H,I') and the view parameters (g_begin, rank).  bf16 arrays are
+    uint16 bit patterns; fp32 arrays are float32.
+    """
+    d = {
+        "x": make_x(cfg, T, seed),
+        "w_gate": make_gate(cfg, seed),
+        "gate_bias": gate_bias(cfg, routing, seed),
+        "routing": routing,
+        "T": T,
+    }
+    if cfg.view == "ep":
+        r = ep_rank_for(cfg, routing, seed) if rank is None else rank
+        E_l = cfg.E // cfg.P
+        d["w13"], d["w2"] = expert_weights(cfg, range(r * E_l, (r + 1) * E_l), seed)
+        d["rank"], d["g_begin"] = r, r * E_l
+    elif cfg.view == "tp":
+        # This GPU's slice of every expert, drawn directly at the slice's shape.
+        Il = cfg.I_local
+        idx = list(range(cfg.E))
+        d["w13"] = _stack(seed, _W13_TP, idx, (2 * Il, cfg.H), cfg.H ** -0.5, cfg.dtype)
+        d["w2"] = _stack(seed, _W2_TP, idx, (cfg.H, Il), cfg.I ** -0.5, cfg.dtype)
+        d["rank"] = 0 if rank is None else rank
+        d["g_begin"] = 0
+    else:
+        w13, w2 = expert_weights(cfg, range(cfg.E), seed)
+        if cfg.n_shared:
+            s13, s2 = shared_weights(cfg, seed)
+            w13 = np.concatenate([w13, s13])
+            w2 = np.concatenate([w2, s2])
+        d["w13"], d["w2"] = w13, w2
+        d["rank"], d["g_begin"] = 0, 0
+    return d
+
+
+def make_full_model(cfg: LayerConfig, T: int, routing: str = "uniform", seed: int = 0) -> dict:
+    """Whole-model weights (every routed expert at full I, plus shared experts).
+
+    Used to build every rank's share of a small model, so that the sum over
+    ranks can be checked against the whole layer.
+    """
+    w13, w2 = expert_weights(cfg, range(cfg.E), seed)
+    if cfg.n_shared:
+        s13, s2 = shared_weights(cfg, seed)
+        w13 = np.concatenate([w13, s13])
+        w2 = np.concatenate([w2, s2])
+    return {
+        "x": make_x(cfg, T, seed),
+        "w_gate": make_gate(cfg, seed),
+        "gate_bias": gate_bias(cfg, routing, seed),
+        "w13": w13,
+        "w2": w2,
+        "routing": routing,
+        "T": T,
+    }
+
+
+def make_repack_inputs(cfg: LayerConfig, seed: int = 0, rank: int = 0) -> dict:
+    """EP-layout expert weights of one rank (its E/P whole experts)."""
+    E_l = cfg.E // cfg.P
+    w13, w2 = expert_weights(cfg, range(rank * E_l, (rank + 1) * E_l), seed)
+    return {"w13_ep": w13, "w2_ep": w2, "rank": rank}
