@@ -1,0 +1,315 @@
+"""Benchmark: MoE-layer forward tokens/s on one MI355X, with the roofline of
+the dominant kernel and the CPU oracle timed beside it.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME --tokens T --routing R]
+    python bench.py --sweep --out results.jsonl     # every batch of the EP/TP/30B workloads
+
+A step is one pass of the whole hot path (gate GEMM + softmax/top-k, permute,
+expert up-projection with SiLU*up, down-projection, combine) over one batch
+of seeded synthetic input already resident in HBM.  Weights are rotated over
+enough bit-identical copies (>= 1 GB in total) that the 256 MB Infinity
+Cache cannot serve them.  Prints ONE JSON line (rank 0; this build runs on
+one GPU only).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s vs batch B at 1 GPU; achieved HBM TB/s (% of peak)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+ROTATE_BYTES = 1.0e9
+DEFAULT = ("dsv2_lite", 256, "uniform")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "expert_up_counters.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=DEFAULT[0])
+    p.add_argument("--tokens", type=int, default=None)
+    p.add_argument("--routing", default=None)
+    p.add_argument("--sweep", action="store_true", help="time every batch of the sweep workloads")
+    p.add_argument("--out", default=None, help="sweep: also append JSON lines to this file")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true", help="also time HIP-graph replay of the step")
+    return p.parse_args()
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("expert_gemm.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "moe_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Workload:
+    """Seeded inputs on the GPU, weights replicated for cache rotation."""
+
+    def __init__(self, name, T, routing):
+        import numpy as np
+        import torch
+
+        from moe_inputs import get_config, make_layer_inputs
+        self.cfg = cfg = get_config(name)
+        self.T, self.routing = T, routing
+        self.host = make_layer_inputs(cfg, T, routing=routing)
+        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+        def dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+            return torch.from_numpy(a).cuda()
+
+        self.x = dev(self.host["x"])
+        self.w_gate = dev(self.host["w_gate"])
+        self.bias = dev(self.host["gate_bias"])
+        w13, w2 = dev(self.host["w13"]), dev(self.host["w2"])
+        wbytes = (w13.numel() + w2.numel()) * w13.element_size()
+        self.copies = max(1, math.ceil(ROTATE_BYTES / wbytes))
+        self.w13 = [w13] + [w13.clone() for _ in range(self.copies - 1)]
+        self.w2 = [w2] + [w2.clone() for _ in range(self.copies - 1)]
+        self.g_begin = self.host["g_begin"]
+        self.dtype = tdt
+        self.elem = 2 if cfg.dtype == "bf16" else 4
+        import moe_layer_amd
+        self.bufs = moe_layer_amd.MoeLayerBuffers.allocate(
+            T, cfg.H, cfg.E, cfg.kk, cfg.n_groups, cfg.I_local, tdt)
+
+    def describe(self):
+        c = self.cfg
+        return {
+            "workload": f"{c.name} T={self.T} {self.routing} ({c.view} view)",
+            "tokens": self.T, "hidden": c.H, "experts": c.E, "top_k": c.k,
+            "renormalised": c.renorm, "shared_experts": c.n_shared, "intermediate_local": c.I_local,
+            "groups_held": c.n_groups, "view": c.view, "ranks_P": c.P, "routing": self.routing,
+            "weight_copies_rotated": self.copies,
+        }
+
+
+def run_step(wl, i, events=None):
+    """One pass of the hot path; optional events bracket each call."""
+    import moe_layer_amd as m
+    c, b = wl.cfg, wl.bufs
+    w13, w2 = wl.w13[i % wl.copies], wl.w2[i % wl.copies]
+    ev = events
+    if ev: ev[0].record()
+    m.moe_route(wl.x, wl.w_gate, wl.bias, c.k, c.renorm, c.n_shared, b.logits, b.topk_ids, b.topk_w)
+    if ev: ev[1].record()
+    m.moe_permute(b.topk_ids, wl.g_begin, c.n_groups, b.counts, b.offsets, b.sorted_pair, b.pair_pos)
+    if ev: ev[2].record()
+    m.moe_expert_up(wl.x, b.sorted_pair, b.offsets, c.kk, w13, b.a)
+    if ev: ev[3].record()
+    m.moe_expert_down(b.a, b.offsets, wl.T, c.kk, w2, b.y_pair)
+    if ev: ev[4].record()
+    m.moe_combine(b.y_pair, b.pair_pos, b.topk_w, b.y)
+    if ev: ev[5].record()
+
+
+def algorithmic(wl):
+    """Bytes and flops the method must move / do (intermediates excluded)."""
+    c, s, T = wl.cfg, wl.elem, wl.T
+    counts = wl.bufs.counts.cpu().numpy()
+    touched = int((counts > 0).sum())
+    kept = int(counts.sum())
+    w13_bytes = touched * 2 * c.I_local * c.H * s
+    w2_bytes = touched * c.H * c.I_local * s
+    layer_bytes = s * c.E * c.H + 2 * s * T * c.H + w13_bytes + w2_bytes
+    layer_flops = 2 * T * c.H * c.E + kept * 6 * c.H * c.I_local
+    up_bytes = w13_bytes + s * T * c.H
+    up_flops = kept * 4 * c.H * c.I_local
+    return dict(touched=touched, kept=kept, layer_bytes=layer_bytes, layer_flops=layer_flops,
+                up_bytes=up_bytes, up_flops=up_flops)
+
+
+def time_workload(wl, steps, warmup, graph=False):
+    import torch
+    for i in range(warmup):
+        run_step(wl, i)
+    torch.cuda.synchronize()
+    # whole-step throughput: K steps between two synchronisations
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run_step(wl, i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / steps
+    # per-kernel durations from events recorded on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        run_step(wl, i, evs[i])
+    torch.cuda.synchronize()
+    names = ("route", "permute", "expert_up", "expert_down", "combine")
+    per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps * 1e3
+           for j, n in enumerate(names)}
+    out = {"t_step_s": t_step, "kernels_us": per}
+    if graph:
+        out["t_step_graph_s"] = time_graph(wl, steps)
+    return out
+
+
+def time_graph(wl, steps):
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run_step(wl, 0)
+    torch.cuda.current_stream().wait_stream(s)
+    graphs = []
+    for c in range(wl.copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_step(wl, c)
+        graphs.append(g)
+    for i in range(3):
+        graphs[i % wl.copies].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % wl.copies].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def measured_traffic(up_launch_bytes):
+    """HBM bytes per up-projection launch from committed rocprofv3 counters,
+    or None when absent or taken on a different kernel source."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha") != kernel_source_sha():
+        return None
+    return (c["fetch_kib"] + c["write_kib"]) * 1024.0 * c["copy_scale"]
+
+
+def cpu_baseline(wl, budget_s=25.0):
+    """The oracle (numpy float64) on the same inputs, on this host's cores."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - reporting only
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    c, d = wl.cfg, wl.host
+    runs, t_total = 0, 0.0
+    while runs == 0 or (t_total < budget_s / 2 and runs < 3):
+        t0 = time.perf_counter()
+        oracle.moe_layer(d["x"], d["w_gate"], d["gate_bias"], d["w13"], d["w2"], c.k, c.renorm,
+                         c.n_shared, d["g_begin"])
+        t_total += time.perf_counter() - t0
+        runs += 1
+    t = t_total / runs
+    return {"value": wl.T / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"whole layer, {wl.T} tokens, {runs} run(s), mean {t:.2f} s per pass "
+                      f"(numpy float64, BLAS threads={cores}, CPUs visible={len(os.sched_getaffinity(0))})"}
+
+
+def report(wl, tm, cpu=None):
+    a = algorithmic(wl)
+    t = tm["t_step_s"]
+    t_up = tm["kernels_us"]["expert_up"] * 1e-6
+    achieved = a["up_bytes"] / t_up / 1e9
+    line = {
+        "metric": METRIC,
+        "value": wl.T / t,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": tm["steps"],
+        "warmup": tm["warmup"],
+        "ms_per_step": t * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights; no trained weights)",
+        "config": wl.describe(),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "expert_up (W13 grouped GEMM + SiLU*up)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": measured_traffic(a["up_bytes"]),
+            "algorithmic_bytes_per_launch": a["up_bytes"],
+        },
+        "layer": {
+            "hbm_achieved_GBs": a["layer_bytes"] / t / 1e9,
+            "hbm_frac": a["layer_bytes"] / t / 1e9 / HBM_PEAK_GBS,
+            "tflops": a["layer_flops"] / t / 1e12,
+            "mfma_frac": a["layer_flops"] / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "algorithmic_bytes": a["layer_bytes"],
+            "touched_groups": a["touched"],
+            "kept_pairs": a["kept"],
+            "kernels_us": {k: round(v, 2) for k, v in tm["kernels_us"].items()},
+        },
+        "cpu_baseline": cpu,
+    }
+    if "t_step_graph_s" in tm:
+        tg = tm["t_step_graph_s"]
+        line["layer"]["graph_replay"] = {"ms_per_step": tg * 1e3, "tokens_per_s": wl.T / tg,
+                                         "hbm_frac": a["layer_bytes"] / tg / 1e9 / HBM_PEAK_GBS}
+    return line
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is described in DESIGN.md, not run.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import moe_layer_amd
+    moe_layer_amd.lib()
+
+    if args.sweep:
+        from moe_inputs import get_config
+        out = open(args.out, "a") if args.out else None
+        for name in ("qwen3_235b_ep", "qwen3_235b_tp", "qwen3_30b"):
+            cfg = get_config(name)
+            for routing in cfg.routing:
+                for T in cfg.T_list:
+                    wl = Workload(name, T, routing)
+                    tm = time_workload(wl, args.steps, args.warmup, graph=args.graph)
+                    tm.update(steps=args.steps, warmup=args.warmup)
+                    line = json.dumps(report(wl, tm))
+                    print(line, flush=True)
+                    if out:
+                        out.write(line + "\n")
+                        out.flush()
+                    del wl
+                    torch.cuda.empty_cache()
+        return
+
+    name = args.workload
+    from moe_inputs import get_config
+    cfg = get_config(name)
+    T = args.tokens or (DEFAULT[1] if name == DEFAULT[0] else cfg.T_list[-1])
+    routing = args.routing or cfg.routing[0]
+    wl = Workload(name, T, routing)
+    tm = time_workload(wl, args.steps, args.warmup, graph=args.graph)
+    tm.update(steps=args.steps, warmup=args.warmup)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+    print(json.dumps(report(wl, tm, cpu)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

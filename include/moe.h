@@ -1,0 +1,165 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer forward-pass library.
+ *
+ * One MoE layer on one GPU's share of the work, in the views of the Moebius
+ * review (§2.1 and §3.1 weight resharding):
+ *   full view : all E routed experts (+ shared experts) held whole;
+ *   EP view   : this rank holds E/P whole experts, W13 (E/P, 2I, H), W2 (E/P, H, I);
+ *   TP view   : this rank holds slice S_p of every expert, W13 (E, 2I/P, H),
+ *               W2 (E, H, I/P); the output is the partial before the all-reduce.
+ * The pass is: gate GEMM, softmax, top-k (moe_route); argsort of the
+ * (token, slot) pairs by expert (moe_permute); the expert FFN
+ * W2 (silu(W1 x) * W3 x) on every kept pair (moe_grouped_gemm); the weighted
+ * sum per token (moe_combine).  moe_repack_ep_to_tp is the local-permute phase
+ * of the EP->TP weight reshard.
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns every
+ *     buffer; the library never allocates or frees, keeps no state between
+ *     calls except a per-device compute-unit count, and only enqueues work on
+ *     `stream` (no host synchronisation).  All calls are graph-capturable.
+ *   - dtype: MOE_DTYPE_F32 or MOE_DTYPE_BF16 is the storage type of activations
+ *     and weights (bf16 = raw bfloat16 bits).  Accumulation is always fp32;
+ *     bf16 results are rounded to nearest even.
+ *   - Row-major, densely packed tensors; every tensor pointer 16-byte aligned.
+ *   - Arguments are checked on the host before anything is enqueued.  On a
+ *     non-zero return nothing was enqueued (MOE_EHIP: the launch itself failed)
+ *     and outputs are unspecified.  Inputs must be finite.
+ *   - T == 0 is valid: moe_permute still writes zero counts and offsets; the
+ *     other calls do nothing.
+ */
+#ifndef MOE_LAYER_AMD_MOE_H
+#define MOE_LAYER_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* null / misaligned pointer, bad dimension, k > E, I % P != 0 ... */
+  MOE_EUNSUPPORTED = 2,  /* shape outside the kernels' tiling limits (see each call) */
+  MOE_EWORKSPACE = 3,    /* workspace missing or smaller than moe_workspace_bytes() */
+  MOE_EHIP = 4           /* the HIP launch reported an error */
+};
+
+enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+
+enum moe_op { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GROUPED_GEMM = 2, MOE_OP_COMBINE = 3,
+              MOE_OP_REPACK = 4 };
+
+/* Version of this ABI (incremented on any signature change). */
+int moe_abi_version(void);
+
+/* Human-readable text for a status code (static storage). */
+const char* moe_status_str(int status);
+
+/* Workspace bytes `op` needs for these sizes (0 if none).  Only
+ * MOE_OP_GROUPED_GEMM uses a workspace: the (T*kk, I) intermediate
+ * activations silu(W1 x) * W3 x in the storage dtype. */
+size_t moe_workspace_bytes(int op, int T, int kk, int n_groups, int H, int I, int dtype);
+
+/*
+ * moe_route -- gate GEMM, softmax and top-k (Sem-MoE notes, Key design 1:
+ * G(h) = top-k(softmax(W_g h + b_g))).
+ *   x          (T, H) dtype          token activations
+ *   w_gate     (E, H) dtype          gate matrix
+ *   gate_bias  (E) fp32, nullable    added to the logits before softmax and top-k
+ *   logits     (T, E) fp32 [out]     x . w_gate^T + b
+ *   topk_ids   (T, k + n_shared) int32 [out]  routed ids in descending logit
+ *              order, ties to the lower id; then shared experts E, E+1, ...
+ *   topk_w     (T, k + n_shared) fp32 [out]   softmax over all E routed experts
+ *              at the picked ids; if renorm != 0, divided by their sum over the
+ *              k picks; shared slots weigh 1.
+ * Limits: 1 <= E <= 512; 1 <= k <= min(E, 32); k + n_shared <= 64;
+ * H * sizeof(dtype) a multiple of 64 and at most 16384 bytes (MOE_EUNSUPPORTED).
+ */
+int moe_route(const void* x, const void* w_gate, const float* gate_bias, int T, int H, int E, int k,
+              int renorm, int n_shared, int dtype, float* logits, int32_t* topk_ids, float* topk_w,
+              hipStream_t stream);
+
+/*
+ * moe_permute -- expert counts, offsets and the stable argsort of the
+ * (token, slot) pairs by expert group (the token reorder of the Sem-MoE
+ * notes, Key design 4).  Pair p = t*kk + j; its group is topk_ids[p] - g_begin
+ * when that lies in [0, n_groups), otherwise the pair is not held here.
+ *   topk_ids    (T, kk) int32
+ *   counts      (n_groups) int32 [out]       pairs per group
+ *   offsets     (n_groups + 1) int32 [out]   exclusive prefix sum; offsets[n_groups] = n_kept
+ *   sorted_pair (T*kk) int32 [out]           first n_kept entries: pair ids in group
+ *                                            order, ascending pair id within a group
+ *   pair_pos    (T*kk) int32 [out]           row of each pair in sorted order, -1 if not held
+ * Views: full / TP: g_begin = 0, n_groups = E + n_shared; EP rank r with
+ * E_l = E/P local experts: g_begin = r*E_l, n_groups = E_l.
+ * Limits: 1 <= kk <= 64; 1 <= n_groups <= 512.  Results are deterministic.
+ */
+int moe_permute(const int32_t* topk_ids, int T, int kk, int g_begin, int n_groups, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t stream);
+
+/*
+ * moe_grouped_gemm -- the expert FFN on every held pair: for sorted row r of
+ * group g (token t = sorted_pair[r] / kk)
+ *     a[r]      = silu(W13[g][0:I] x_t) * (W13[g][I:2I] x_t),  silu(z) = z/(1+e^-z)
+ *     y_pair[r] = W2[g] a[r]
+ * (Moebius review, §3.1: W13 (., 2I, H) and W2 (., H, I); gate rows first.)
+ *   x           (T, H) dtype
+ *   sorted_pair, offsets   from moe_permute
+ *   w13         (n_groups, 2I, H) dtype   I = this GPU's intermediate size (I/P in TP)
+ *   w2          (n_groups, H, I) dtype
+ *   y_pair      (T*kk, H) dtype [out]     first n_kept rows written
+ *   ws          >= moe_workspace_bytes(MOE_OP_GROUPED_GEMM, ...) bytes, holds a
+ * Limits: H * sizeof(dtype) a multiple of 64 and <= 16384 bytes; H % 16 == 0;
+ * I * sizeof(dtype) a multiple of 64 and <= 16384 bytes; n_groups <= 512.
+ * a is rounded to dtype before the W2 product.
+ */
+int moe_grouped_gemm(const void* x, const int32_t* sorted_pair, const int32_t* offsets, int T, int kk,
+                     int n_groups, const void* w13, const void* w2, int H, int I, int dtype,
+                     void* y_pair, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The two halves of moe_grouped_gemm, for callers that keep `a` themselves.
+ * moe_expert_up writes a (T*kk, I) dtype; moe_expert_down reads it.  Same
+ * limits as moe_grouped_gemm. */
+int moe_expert_up(const void* x, const int32_t* sorted_pair, const int32_t* offsets, int T, int kk,
+                  int n_groups, const void* w13, int H, int I, int dtype, void* a,
+                  hipStream_t stream);
+int moe_expert_down(const void* a, const int32_t* offsets, int T, int kk, int n_groups,
+                    const void* w2, int H, int I, int dtype, void* y_pair, hipStream_t stream);
+
+/*
+ * moe_combine -- y[t] = sum_{j=0..kk-1, in order, pair_pos[t*kk+j] >= 0}
+ *                       topk_w[t*kk+j] * y_pair[pair_pos[t*kk+j]]
+ * fp32 accumulation, one rounding to dtype; rows with no held pair are 0.
+ * This is the EP rank's partial before the combine all-to-all, or the TP
+ * rank's partial before the all-reduce (Moebius review, §2.1).
+ *   y_pair (T*kk, H) dtype, pair_pos (T*kk) int32, topk_w (T*kk) fp32,
+ *   y (T, H) dtype [out].   Limit: H * sizeof(dtype) a multiple of 16.
+ */
+int moe_combine(const void* y_pair, const int32_t* pair_pos, const float* topk_w, int T, int kk, int H,
+                int dtype, void* y, hipStream_t stream);
+
+/*
+ * moe_repack_ep_to_tp -- local-permute phase of the EP->TP expert-weight
+ * reshard (Moebius review, §3.1 and Fig. 4): pack this rank's E_local whole
+ * experts into one contiguous block per destination peer q < P:
+ *   dst13[q] (E_local, 2I/P, H) = rows [q I/P, (q+1) I/P) of the gate half, then
+ *                                 the same rows of the up half, of each expert
+ *   dst2[q]  (E_local, H, I/P)  = columns [q I/P, (q+1) I/P) of each W2 row
+ *   w13_ep (E_local, 2I, H), w2_ep (E_local, H, I) dtype, exact byte copies.
+ *   dst13, dst2: HOST arrays of P device pointers (blocks must not overlap the
+ *   sources or each other).  A peer-mapped pointer works the same way.
+ * Limits: 1 <= P <= 64; I % P == 0; (I/P) * sizeof(dtype) and H * sizeof(dtype)
+ * multiples of 16.
+ */
+int moe_repack_ep_to_tp(const void* w13_ep, const void* w2_ep, int E_local, int H, int I, int P,
+                        int dtype, void* const* dst13, void* const* dst2, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYER_AMD_MOE_H */

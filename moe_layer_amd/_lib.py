@@ -1,0 +1,197 @@
+"""ctypes binding of libmoe_layer_amd.so: argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU (torch is
+used for device memory and streams), checks their dtype, shape and
+contiguity, and passes raw pointers and sizes to the C entry point of the
+same name on the current torch stream.  No computation happens here and
+there is no fallback: if the HIP library is missing, loading fails.
+"""
+import ctypes
+import os
+
+import torch  # noqa: F401  (must load first: the library shares torch's HIP runtime)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_layer_amd.so")
+
+MOE_DTYPE_F32 = 0
+MOE_DTYPE_BF16 = 1
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM, MOE_OP_COMBINE, MOE_OP_REPACK = range(5)
+
+EXPORTED = (
+    "moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
+    "moe_grouped_gemm", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_repack_ep_to_tp",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+def lib():
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"HIP library not found at {LIB_PATH}; build it with "
+            "`python -m moe_layer_amd.build` (or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    L.moe_abi_version.restype = _i
+    L.moe_abi_version.argtypes = []
+    L.moe_status_str.restype = ctypes.c_char_p
+    L.moe_status_str.argtypes = [_i]
+    L.moe_workspace_bytes.restype = _sz
+    L.moe_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+    L.moe_route.restype = _i
+    L.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p]
+    L.moe_permute.restype = _i
+    L.moe_permute.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p]
+    L.moe_grouped_gemm.restype = _i
+    L.moe_grouped_gemm.argtypes = [_p, _p, _p, _i, _i, _i, _p, _p, _i, _i, _i, _p, _p, _sz, _p]
+    L.moe_expert_up.restype = _i
+    L.moe_expert_up.argtypes = [_p, _p, _p, _i, _i, _i, _p, _i, _i, _i, _p, _p]
+    L.moe_expert_down.restype = _i
+    L.moe_expert_down.argtypes = [_p, _p, _i, _i, _i, _p, _i, _i, _i, _p, _p]
+    L.moe_combine.restype = _i
+    L.moe_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p]
+    L.moe_repack_ep_to_tp.restype = _i
+    L.moe_repack_ep_to_tp.argtypes = [_p, _p, _i, _i, _i, _i, _i, ctypes.POINTER(_p),
+                                      ctypes.POINTER(_p), _p]
+    _lib = L
+    return L
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MoeError(fn, status, lib().moe_status_str(status).decode())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return MOE_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return MOE_DTYPE_F32
+    raise TypeError(f"unsupported storage dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t, name, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def abi_version():
+    return lib().moe_abi_version()
+
+
+def moe_workspace_bytes(op, T, kk, n_groups, H, I, dtype_code):
+    return lib().moe_workspace_bytes(op, T, kk, n_groups, H, I, dtype_code)
+
+
+def moe_route(x, w_gate, gate_bias, k, renorm, n_shared, logits, topk_ids, topk_w, stream=None):
+    T, H = x.shape
+    E = w_gate.shape[0]
+    kk = k + n_shared
+    dt = _dtype_code(x)
+    st = lib().moe_route(
+        _ptr(x, "x"), _ptr(w_gate, "w_gate", x.dtype, (E, H)),
+        _ptr(gate_bias, "gate_bias", torch.float32, (E,)), T, H, E, k, int(bool(renorm)), n_shared,
+        dt, _ptr(logits, "logits", torch.float32, (T, E)),
+        _ptr(topk_ids, "topk_ids", torch.int32, (T, kk)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, kk)), _stream(stream))
+    _check("moe_route", st)
+
+
+def moe_permute(topk_ids, g_begin, n_groups, counts, offsets, sorted_pair, pair_pos, stream=None):
+    T, kk = topk_ids.shape
+    st = lib().moe_permute(
+        _ptr(topk_ids, "topk_ids", torch.int32), T, kk, g_begin, n_groups,
+        _ptr(counts, "counts", torch.int32, (n_groups,)),
+        _ptr(offsets, "offsets", torch.int32, (n_groups + 1,)),
+        _ptr(sorted_pair, "sorted_pair", torch.int32, (T * kk,)),
+        _ptr(pair_pos, "pair_pos", torch.int32, (T * kk,)), _stream(stream))
+    _check("moe_permute", st)
+
+
+def moe_grouped_gemm(x, sorted_pair, offsets, kk, w13, w2, y_pair, ws, stream=None):
+    T, H = x.shape
+    G, two_i, _ = w13.shape
+    I = two_i // 2
+    dt = _dtype_code(x)
+    st = lib().moe_grouped_gemm(
+        _ptr(x, "x"), _ptr(sorted_pair, "sorted_pair", torch.int32, (T * kk,)),
+        _ptr(offsets, "offsets", torch.int32, (G + 1,)), T, kk, G,
+        _ptr(w13, "w13", x.dtype, (G, 2 * I, H)), _ptr(w2, "w2", x.dtype, (G, H, I)), H, I, dt,
+        _ptr(y_pair, "y_pair", x.dtype, (T * kk, H)), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _check("moe_grouped_gemm", st)
+
+
+def moe_expert_up(x, sorted_pair, offsets, kk, w13, a, stream=None):
+    T, H = x.shape
+    G, two_i, _ = w13.shape
+    I = two_i // 2
+    st = lib().moe_expert_up(
+        _ptr(x, "x"), _ptr(sorted_pair, "sorted_pair", torch.int32, (T * kk,)),
+        _ptr(offsets, "offsets", torch.int32, (G + 1,)), T, kk, G,
+        _ptr(w13, "w13", x.dtype, (G, 2 * I, H)), H, I, _dtype_code(x),
+        _ptr(a, "a", x.dtype, (T * kk, I)), _stream(stream))
+    _check("moe_expert_up", st)
+
+
+def moe_expert_down(a, offsets, T, kk, w2, y_pair, stream=None):
+    G, H, I = w2.shape
+    st = lib().moe_expert_down(
+        _ptr(a, "a", w2.dtype, (T * kk, I)), _ptr(offsets, "offsets", torch.int32, (G + 1,)), T, kk, G,
+        _ptr(w2, "w2"), H, I, _dtype_code(w2), _ptr(y_pair, "y_pair", w2.dtype, (T * kk, H)),
+        _stream(stream))
+    _check("moe_expert_down", st)
+
+
+def moe_combine(y_pair, pair_pos, topk_w, y, stream=None):
+    T, H = y.shape
+    kk = topk_w.shape[1]
+    st = lib().moe_combine(
+        _ptr(y_pair, "y_pair", y.dtype), _ptr(pair_pos, "pair_pos", torch.int32, (T * kk,)),
+        _ptr(topk_w, "topk_w", torch.float32, (T, kk)), T, kk, H, _dtype_code(y), _ptr(y, "y"),
+        _stream(stream))
+    _check("moe_combine", st)
+
+
+def moe_repack_ep_to_tp(w13_ep, w2_ep, P, dst13, dst2, stream=None):
+    E_l, two_i, H = w13_ep.shape
+    I = two_i // 2
+    if len(dst13) != P or len(dst2) != P:
+        raise ValueError("need P destination blocks for each tensor")
+    Ip = I // P
+    arr13 = (_p * P)(*[_ptr(d, f"dst13[{q}]", w13_ep.dtype, (E_l, 2 * Ip, H)) for q, d in enumerate(dst13)])
+    arr2 = (_p * P)(*[_ptr(d, f"dst2[{q}]", w13_ep.dtype, (E_l, H, Ip)) for q, d in enumerate(dst2)])
+    st = lib().moe_repack_ep_to_tp(
+        _ptr(w13_ep, "w13_ep"), _ptr(w2_ep, "w2_ep", w13_ep.dtype, (E_l, H, I)), E_l, H, I, P,
+        _dtype_code(w13_ep), arr13, arr2, _stream(stream))
+    _check("moe_repack_ep_to_tp", st)

@@ -1,0 +1,108 @@
+// Device helpers shared by the MoE-layer kernels (gfx950 / CDNA4, wave64).
+//
+// Operand fragments.  Every contraction here has its K dimension contiguous
+// in memory for both operands (weight rows and activation rows), so one lane
+// loads one 16-byte chunk of a row straight into the register layout of a
+// 16x16 MFMA: lane l holds row (l % 16), bytes [16*(l/16), 16*(l/16)+16) of a
+// 64-byte K-chunk.  For bf16 that chunk is the 8 K-values the
+// v_mfma_f32_16x16x32_bf16 operand wants from a lane; for fp32 it is four
+// K-values consumed by four v_mfma_f32_16x16x4_f32 steps.  Both operands use
+// the same byte->K mapping, so the K-sum is complete and exact in order-free
+// terms.  The 16x16 fp32 result sits in lane l as rows 4*(l/16)+r, r = 0..3,
+// column l % 16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr int FRAG_BYTES = 64;  // bytes of K covered per row by one fragment step
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<uint16_t> {  // bf16 storage
+  static constexpr int bytes = 2;
+  __device__ __forceinline__ static f32x4_t mma(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  // Store 4 consecutive values.
+  __device__ __forceinline__ static void store4(uint16_t* p, float a, float b, float c, float d) {
+    uint2 v;
+    v.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    v.y = static_cast<uint32_t>(f32_to_bf16(c)) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
+    *reinterpret_cast<uint2*>(p) = v;
+  }
+};
+
+template <>
+struct Elem<float> {
+  static constexpr int bytes = 4;
+  __device__ __forceinline__ static f32x4_t mma(uint4 a, uint4 b, f32x4_t c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    return c;
+  }
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  }
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+
+// Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele with shuffles).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    int o = __shfl_up(v, d, WAVE);
+    if (l >= d) v += o;
+  }
+  return v;
+}
+
+// Build, in LDS, the list of expert groups that received at least one pair and
+// the number of such groups.  Run by wave 0 of the block; `list` must hold
+// n_groups entries.  The list is in ascending group order.
+__device__ __forceinline__ void touched_groups(const int* __restrict__ offsets, int n_groups,
+                                               int* list, int* n_list) {
+  if (threadIdx.x >= WAVE) return;
+  const int l = lane_id();
+  int base = 0;
+  for (int g0 = 0; g0 < n_groups; g0 += WAVE) {
+    const int g = g0 + l;
+    int used = 0;
+    if (g < n_groups) used = (offsets[g + 1] - offsets[g]) > 0;
+    const int incl = wave_inclusive_scan(used);
+    if (used) list[base + incl - 1] = g;
+    base += __shfl(incl, WAVE - 1, WAVE);
+  }
+  if (l == 0) *n_list = base;
+}
+
+}  // namespace moe

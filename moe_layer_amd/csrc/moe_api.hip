@@ -1,0 +1,159 @@
+// The exported C ABI (declared in include/moe.h): host-side argument checks,
+// then the launches.  Nothing here allocates, frees or synchronises.
+#include "moe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int ABI_VERSION = 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+int elem_bytes(int dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+bool dtype_ok(int dtype) { return dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16; }
+
+// A contraction length the fragment kernels take: whole 64-byte K-chunks,
+// at most MAX_KSPLIT waves of 16 chunks.
+bool k_len_ok(int K, int dtype) {
+  const long long b = static_cast<long long>(K) * elem_bytes(dtype);
+  return b % 64 == 0 && b <= 64LL * 16 * MAX_KSPLIT;
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+int check_gemm_shapes(int T, int kk, int n_groups, int H, int I, int dtype) {
+  if (T < 0 || kk < 1 || kk > MAX_KK || n_groups < 1 || H < 1 || I < 1 || !dtype_ok(dtype))
+    return MOE_EINVAL;
+  if (n_groups > MAX_GROUPS) return MOE_EUNSUPPORTED;
+  if (!k_len_ok(H, dtype) || H % 16 != 0) return MOE_EUNSUPPORTED;
+  if (!k_len_ok(I, dtype) || I % 8 != 0) return MOE_EUNSUPPORTED;
+  if (static_cast<long long>(T) * kk > (1LL << 30)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument (null or misaligned pointer, bad dimension)";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: shape outside the kernels' tiling limits";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace missing or too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP kernel launch failed";
+    default: return "unknown moe status";
+  }
+}
+
+size_t moe_workspace_bytes(int op, int T, int kk, int n_groups, int H, int I, int dtype) {
+  (void)n_groups;
+  (void)H;
+  if (op != MOE_OP_GROUPED_GEMM || T <= 0 || kk <= 0 || I <= 0 || !dtype_ok(dtype)) return 0;
+  const size_t b = static_cast<size_t>(T) * kk * I * elem_bytes(dtype);
+  return (b + 255) & ~static_cast<size_t>(255);
+}
+
+int moe_route(const void* x, const void* w_gate, const float* gate_bias, int T, int H, int E, int k,
+              int renorm, int n_shared, int dtype, float* logits, int32_t* topk_ids, float* topk_w,
+              hipStream_t stream) {
+  if (T < 0 || H < 1 || E < 1 || k < 1 || n_shared < 0 || k > E || !dtype_ok(dtype)) return MOE_EINVAL;
+  if (E > MAX_E || k > MAX_K || k + n_shared > MAX_KK || !k_len_ok(H, dtype)) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_gate || !logits || !topk_ids || !topk_w) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned4(logits) || !aligned4(topk_ids) ||
+      !aligned4(topk_w) || (gate_bias && !aligned4(gate_bias)))
+    return MOE_EINVAL;
+  launch_gate_gemm(dtype, x, w_gate, gate_bias, logits, T, H, E, stream);
+  launch_topk(logits, T, E, k, renorm ? 1 : 0, n_shared, topk_ids, topk_w, stream);
+  return launched();
+}
+
+int moe_permute(const int32_t* topk_ids, int T, int kk, int g_begin, int n_groups, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t stream) {
+  if (T < 0 || kk < 1 || kk > MAX_KK || g_begin < 0 || n_groups < 1) return MOE_EINVAL;
+  if (n_groups > MAX_GROUPS || static_cast<long long>(T) * kk > (1LL << 30)) return MOE_EUNSUPPORTED;
+  if (!counts || !offsets || !aligned4(counts) || !aligned4(offsets)) return MOE_EINVAL;
+  if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos || !aligned4(topk_ids) ||
+                !aligned4(sorted_pair) || !aligned4(pair_pos)))
+    return MOE_EINVAL;
+  launch_permute(topk_ids, T, kk, g_begin, n_groups, counts, offsets, sorted_pair, pair_pos, stream);
+  return launched();
+}
+
+int moe_expert_up(const void* x, const int32_t* sorted_pair, const int32_t* offsets, int T, int kk,
+                  int n_groups, const void* w13, int H, int I, int dtype, void* a,
+                  hipStream_t stream) {
+  const int st = check_gemm_shapes(T, kk, n_groups, H, I, dtype);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !sorted_pair || !offsets || !w13 || !a) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(a) || !aligned4(sorted_pair) || !aligned4(offsets))
+    return MOE_EINVAL;
+  launch_expert_up(dtype, x, sorted_pair, offsets, n_groups, T, kk, w13, H, I, a, stream);
+  return launched();
+}
+
+int moe_expert_down(const void* a, const int32_t* offsets, int T, int kk, int n_groups,
+                    const void* w2, int H, int I, int dtype, void* y_pair, hipStream_t stream) {
+  const int st = check_gemm_shapes(T, kk, n_groups, H, I, dtype);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!a || !offsets || !w2 || !y_pair) return MOE_EINVAL;
+  if (!aligned16(a) || !aligned16(w2) || !aligned16(y_pair) || !aligned4(offsets)) return MOE_EINVAL;
+  launch_expert_down(dtype, a, offsets, n_groups, T, kk, w2, H, I, y_pair, stream);
+  return launched();
+}
+
+int moe_grouped_gemm(const void* x, const int32_t* sorted_pair, const int32_t* offsets, int T, int kk,
+                     int n_groups, const void* w13, const void* w2, int H, int I, int dtype,
+                     void* y_pair, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int st = check_gemm_shapes(T, kk, n_groups, H, I, dtype);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !sorted_pair || !offsets || !w13 || !w2 || !y_pair) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(y_pair) ||
+      !aligned4(sorted_pair) || !aligned4(offsets))
+    return MOE_EINVAL;
+  if (!ws || !aligned16(ws) || ws_bytes < moe_workspace_bytes(MOE_OP_GROUPED_GEMM, T, kk, n_groups, H, I, dtype))
+    return MOE_EWORKSPACE;
+  launch_expert_up(dtype, x, sorted_pair, offsets, n_groups, T, kk, w13, H, I, ws, stream);
+  launch_expert_down(dtype, ws, offsets, n_groups, T, kk, w2, H, I, y_pair, stream);
+  return launched();
+}
+
+int moe_combine(const void* y_pair, const int32_t* pair_pos, const float* topk_w, int T, int kk, int H,
+                int dtype, void* y, hipStream_t stream) {
+  if (T < 0 || kk < 1 || kk > MAX_KK || H < 1 || !dtype_ok(dtype)) return MOE_EINVAL;
+  if ((static_cast<long long>(H) * elem_bytes(dtype)) % 16 != 0) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_pair || !pair_pos || !topk_w || !y) return MOE_EINVAL;
+  if (!aligned16(y_pair) || !aligned16(y) || !aligned4(pair_pos) || !aligned4(topk_w)) return MOE_EINVAL;
+  launch_combine(dtype, y_pair, pair_pos, topk_w, T, kk, H, y, stream);
+  return launched();
+}
+
+int moe_repack_ep_to_tp(const void* w13_ep, const void* w2_ep, int E_local, int H, int I, int P,
+                        int dtype, void* const* dst13, void* const* dst2, hipStream_t stream) {
+  if (E_local < 1 || H < 1 || I < 1 || P < 1 || !dtype_ok(dtype)) return MOE_EINVAL;
+  if (I % P != 0) return MOE_EINVAL;
+  if (P > MAX_P) return MOE_EUNSUPPORTED;
+  const int eb = elem_bytes(dtype);
+  if ((static_cast<long long>(I / P) * eb) % 16 != 0 || (static_cast<long long>(H) * eb) % 16 != 0)
+    return MOE_EUNSUPPORTED;
+  if (!w13_ep || !w2_ep || !dst13 || !dst2 || !aligned16(w13_ep) || !aligned16(w2_ep)) return MOE_EINVAL;
+  PeerPtrs d13{}, d2{};
+  for (int q = 0; q < P; ++q) {
+    if (!dst13[q] || !dst2[q] || !aligned16(dst13[q]) || !aligned16(dst2[q])) return MOE_EINVAL;
+    d13.p[q] = dst13[q];
+    d2.p[q] = dst2[q];
+  }
+  launch_repack_ep_to_tp(dtype, w13_ep, w2_ep, E_local, H, I, P, d13, d2, stream);
+  return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal launcher interface between the C-ABI layer (moe_api.hip) and the
+// kernel files.  Every launcher assumes its arguments were validated by the
+// C-ABI layer and only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Limits shared by the host checks and the kernels.
+constexpr int MAX_GROUPS = 512;   // expert groups per call (LDS tables)
+constexpr int MAX_E = 512;        // routed experts in the gate (8 logits per lane)
+constexpr int MAX_K = 32;         // routed picks per token
+constexpr int MAX_KK = 64;        // routed + shared slots per token
+constexpr int MAX_P = 64;         // peers in a repack
+constexpr int MAX_KSPLIT = 16;    // waves splitting K inside one block
+
+int device_cu_count();
+
+// gate GEMM: logits (T,E) fp32 = x (T,H) . Wg (E,H)^T + b
+void launch_gate_gemm(int dtype, const void* x, const void* wg, const float* bias, float* logits,
+                      int T, int H, int E, hipStream_t s);
+// softmax + top-k (+ renorm, + shared slots)
+void launch_topk(const float* logits, int T, int E, int k, int renorm, int n_shared,
+                 int32_t* ids, float* w, hipStream_t s);
+// counts, offsets, stable permutation
+void launch_permute(const int32_t* ids, int T, int kk, int g_begin, int n_groups, int32_t* counts,
+                    int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s);
+// expert up-projection with SiLU(gate)*up epilogue -> A (n_pairs, I)
+void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, const int32_t* offsets,
+                      int n_groups, int T, int kk, const void* w13, int H, int I, void* a,
+                      hipStream_t s);
+// expert down-projection -> y_pair (n_pairs, H)
+void launch_expert_down(int dtype, const void* a, const int32_t* offsets, int n_groups, int T,
+                        int kk, const void* w2, int H, int I, void* y_pair, hipStream_t s);
+// weighted combine -> y (T, H)
+void launch_combine(int dtype, const void* y_pair, const int32_t* pair_pos, const float* w, int T,
+                    int kk, int H, void* y, hipStream_t s);
+
+struct PeerPtrs {
+  void* p[MAX_P];
+};
+// EP -> TP local permute of expert weights into P per-peer blocks
+void launch_repack_ep_to_tp(int dtype, const void* w13, const void* w2, int E_local, int H, int I,
+                            int P, const PeerPtrs& d13, const PeerPtrs& d2, hipStream_t s);
+
+}  // namespace moe

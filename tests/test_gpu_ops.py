@@ -1,0 +1,234 @@
+"""GPU parity on edge cases and properties: ragged and tiny batches, empty
+EP shares, ties, arbitrary permutation inputs, the repack at small shapes,
+the sum over ranks of the EP and TP shares, determinism and graph replay."""
+import numpy as np
+import pytest
+
+import oracle
+from moe_inputs import LayerConfig, make_full_model, make_layer_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def small(H=256, E=16, k=4, I=128, renorm=True, n_shared=0, dtype="bf16", view="full", P=1, T=37):
+    return LayerConfig(name="small", H=H, E=E, k=k, renorm=renorm, I=I, dtype=dtype, T_list=(T,),
+                       n_shared=n_shared, view=view, P=P)
+
+
+@pytest.mark.parametrize("T", [1, 2, 15, 17, 37, 100])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_ragged_batches(T, dtype):
+    import gpu_helpers as gh
+    cfg = small(dtype=dtype, T=T)
+    d = make_layer_inputs(cfg, T, routing="uniform", seed=T)
+    print(f"[case] ragged T={T} {dtype}", flush=True)
+    gh.check_layer(d, cfg, gh.gpu_layer(d, cfg))
+
+
+@pytest.mark.parametrize("n_shared,renorm", [(2, False), (1, True)])
+def test_shared_experts(n_shared, renorm):
+    import gpu_helpers as gh
+    cfg = small(n_shared=n_shared, renorm=renorm, T=40)
+    d = make_layer_inputs(cfg, 40, seed=1)
+    print(f"[case] shared n_shared={n_shared}", flush=True)
+    gh.check_layer(d, cfg, gh.gpu_layer(d, cfg))
+
+
+def test_k_equals_E():
+    import gpu_helpers as gh
+    cfg = small(E=8, k=8, T=20)
+    d = make_layer_inputs(cfg, 20, seed=2)
+    print("[case] k=E", flush=True)
+    gh.check_layer(d, cfg, gh.gpu_layer(d, cfg))
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_all_logits_tied(renorm):
+    import gpu_helpers as gh
+    cfg = small(renorm=renorm, T=24)
+    d = make_layer_inputs(cfg, 24, seed=3)
+    d["w_gate"] = np.zeros_like(d["w_gate"])
+    print("[case] tied logits", flush=True)
+    g = gh.gpu_layer(d, cfg)
+    assert (g["topk_ids"] == np.arange(cfg.k)).all()
+    assert np.allclose(g["topk_w"], 1 / cfg.k if renorm else 1 / cfg.E, atol=1e-7)
+    assert g["counts"].tolist() == [24] * cfg.k + [0] * (cfg.E - cfg.k)
+    gh.check_layer(d, cfg, g, expect_near_ties=24)
+
+
+def test_bias_ties_and_signed_zero():
+    import gpu_helpers as gh
+    cfg = small(E=16, k=4, T=8)
+    d = make_layer_inputs(cfg, 8, seed=4)
+    d["w_gate"] = np.zeros_like(d["w_gate"])
+    b = np.zeros(16, dtype=np.float32)
+    b[[3, 9]] = 2.0        # tie at the top: 3 before 9
+    b[[5, 6, 12]] = 1.0    # three-way tie for two places: 5 and 6
+    b[7] = -0.0
+    d["gate_bias"] = b
+    print("[case] bias ties", flush=True)
+    g = gh.gpu_layer(d, cfg)
+    assert (g["topk_ids"] == [3, 9, 5, 6]).all()
+
+
+def test_ep_rank_with_no_local_pairs():
+    import gpu_helpers as gh
+    cfg = small(E=16, k=2, view="ep", P=4, T=12)
+    d = make_layer_inputs(cfg, 12, rank=3, seed=5)
+    b = np.zeros(16, dtype=np.float32)
+    b[:4] = 50.0           # everything goes to rank 0's experts
+    d["gate_bias"] = b
+    print("[case] empty EP share", flush=True)
+    g = gh.gpu_layer(d, cfg)
+    assert g["counts"].sum() == 0 and (g["pair_pos"] == -1).all()
+    assert (oracle.widen(g["y"]) == 0).all()
+    gh.check_layer(d, cfg, g)
+
+
+def test_permute_arbitrary_ids():
+    import torch
+
+    import gpu_helpers as gh
+    import moe_layer_amd
+    rng = np.random.default_rng(11)
+    for T, kk, g_begin, n_groups in [(1000, 7, 5, 40), (3, 1, 0, 1), (2048, 8, 0, 130), (64, 64, 100, 7)]:
+        ids = rng.integers(-3, g_begin + n_groups + 5, size=(T, kk)).astype(np.int32)
+        print(f"[case] permute T={T} kk={kk} window=({g_begin},{n_groups})", flush=True)
+        dev = gh.to_dev(ids)
+        out = [torch.empty(s, dtype=torch.int32, device="cuda") for s in
+               (n_groups, n_groups + 1, T * kk, T * kk)]
+        moe_layer_amd.moe_permute(dev, g_begin, n_groups, *out)
+        torch.cuda.synchronize()
+        c, o, sp, pos = oracle.permute(ids, g_begin, n_groups)
+        got = [gh.from_dev(t) for t in out]
+        assert np.array_equal(got[0], c) and np.array_equal(got[1], o)
+        assert np.array_equal(got[2][:o[-1]], sp) and np.array_equal(got[3], pos)
+
+
+def test_permute_empty_batch_writes_zero_counts():
+    import torch
+
+    import moe_layer_amd
+    counts = torch.full((9,), 7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((10,), 7, dtype=torch.int32, device="cuda")
+    ids = torch.empty((0, 4), dtype=torch.int32, device="cuda")
+    e = torch.empty((0,), dtype=torch.int32, device="cuda")
+    moe_layer_amd.moe_permute(ids, 0, 9, counts, offsets, e, e)
+    torch.cuda.synchronize()
+    assert counts.cpu().tolist() == [0] * 9 and offsets.cpu().tolist() == [0] * 10
+
+
+@pytest.mark.parametrize("dtype,P,E_l,H,I", [
+    ("bf16", 1, 2, 256, 64), ("bf16", 2, 3, 128, 64), ("bf16", 8, 2, 512, 128),
+    ("fp32", 4, 3, 64, 32), ("bf16", 16, 1, 64, 128),
+])
+def test_repack_small(dtype, P, E_l, H, I):
+    import torch
+
+    import gpu_helpers as gh
+    import moe_layer_amd
+    rng = np.random.default_rng(P)
+    if dtype == "bf16":
+        w13 = rng.integers(0, 65535, size=(E_l, 2 * I, H), dtype=np.uint16)
+        w2 = rng.integers(0, 65535, size=(E_l, H, I), dtype=np.uint16)
+        # keep the bit patterns finite-valued (no NaN/Inf exponent)
+        w13 &= 0xBFFF
+        w2 &= 0xBFFF
+        tdt = torch.bfloat16
+    else:
+        w13 = rng.standard_normal((E_l, 2 * I, H)).astype(np.float32)
+        w2 = rng.standard_normal((E_l, H, I)).astype(np.float32)
+        tdt = torch.float32
+    Ip = I // P
+    print(f"[case] repack {dtype} P={P}", flush=True)
+    d13 = [torch.empty((E_l, 2 * Ip, H), dtype=tdt, device="cuda") for _ in range(P)]
+    d2 = [torch.empty((E_l, H, Ip), dtype=tdt, device="cuda") for _ in range(P)]
+    moe_layer_amd.moe_repack_ep_to_tp(gh.to_dev(w13), gh.to_dev(w2), P, d13, d2)
+    torch.cuda.synchronize()
+    b13, b2 = oracle.repack_ep_to_tp(w13, w2, P)
+    for q in range(P):
+        assert np.array_equal(gh.from_dev(d13[q]), b13[q])
+        assert np.array_equal(gh.from_dev(d2[q]), b2[q])
+
+
+@pytest.mark.parametrize("routing", ["uniform", "zipf"])
+def test_sum_of_rank_shares_is_the_full_layer(routing):
+    """All P EP shares and all P TP shares of one model on this GPU; the TP
+    weights are built by the GPU repack of each EP rank's experts."""
+    import torch
+
+    import gpu_helpers as gh
+    import moe_layer_amd
+    P, T = 8, 96
+    cfg = LayerConfig(name="ranks", H=512, E=32, k=4, renorm=True, I=256, dtype="bf16", T_list=(T,))
+    m = make_full_model(cfg, T, routing=routing, seed=21)
+    full = oracle.moe_layer(m["x"], m["w_gate"], m["gate_bias"], m["w13"], m["w2"], cfg.k, cfg.renorm)
+    E_l, Ip = cfg.E // P, cfg.I // P
+    x, wg, b = gh.to_dev(m["x"]), gh.to_dev(m["w_gate"]), gh.to_dev(m["gate_bias"])
+    w13_all, w2_all = gh.to_dev(m["w13"]), gh.to_dev(m["w2"])
+    print(f"[case] rank shares {routing}", flush=True)
+    ep_sum = np.zeros((T, cfg.H))
+    tp13 = [torch.empty((cfg.E, 2 * Ip, cfg.H), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    tp2 = [torch.empty((cfg.E, cfg.H, Ip), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    for r in range(P):
+        sl = slice(r * E_l, (r + 1) * E_l)
+        w13_r, w2_r = w13_all[sl].contiguous(), w2_all[sl].contiguous()
+        bufs = moe_layer_amd.moe_layer_forward(x, wg, b, w13_r, w2_r, cfg.k, cfg.renorm, 0, r * E_l)
+        ep_sum += oracle.widen(gh.from_dev(bufs.y))
+        # rank r's repack writes rows G_r of every peer's TP tensors
+        moe_layer_amd.moe_repack_ep_to_tp(w13_r, w2_r, P, [t[sl] for t in tp13], [t[sl] for t in tp2])
+    tp_sum = np.zeros((T, cfg.H))
+    for p in range(P):
+        bufs = moe_layer_amd.moe_layer_forward(x, wg, b, tp13[p], tp2[p], cfg.k, cfg.renorm)
+        tp_sum += oracle.widen(gh.from_dev(bufs.y))
+        want13, want2 = oracle.tp_slice(m["w13"], m["w2"], p, P)
+        assert np.array_equal(gh.from_dev(tp13[p]), want13)
+        assert np.array_equal(gh.from_dev(tp2[p]), want2)
+    torch.cuda.synchronize()
+    gh.assert_close(ep_sum, full["y"], "bf16", "sum of EP shares")
+    gh.assert_close(tp_sum, full["y"], "bf16", "sum of TP shares")
+
+
+def test_repeated_runs_are_bit_identical():
+    import gpu_helpers as gh
+    cfg = small(E=64, k=6, T=200, n_shared=2, renorm=False)
+    d = make_layer_inputs(cfg, 200, seed=6)
+    print("[case] determinism", flush=True)
+    a = gh.gpu_layer(d, cfg)
+    b = gh.gpu_layer(d, cfg)
+    for key in a:
+        n = int(a["offsets"][-1])
+        va, vb = (a[key][:n], b[key][:n]) if key in ("sorted_pair", "a", "y_pair") else (a[key], b[key])
+        assert np.array_equal(va, vb), key
+
+
+def test_graph_replay_matches_eager():
+    import torch
+
+    import gpu_helpers as gh
+    import moe_layer_amd
+    cfg = small(E=32, k=4, T=64)
+    d = make_layer_inputs(cfg, 64, seed=8)
+    x, wg, b = gh.to_dev(d["x"]), gh.to_dev(d["w_gate"]), gh.to_dev(d["gate_bias"])
+    w13, w2 = gh.to_dev(d["w13"]), gh.to_dev(d["w2"])
+    print("[case] graph replay", flush=True)
+    eager = moe_layer_amd.moe_layer_forward(x, wg, b, w13, w2, cfg.k, cfg.renorm)
+    torch.cuda.synchronize()
+    want = gh.from_dev(eager.y).copy()
+    bufs = moe_layer_amd.MoeLayerBuffers.allocate(64, cfg.H, cfg.E, cfg.k, cfg.E, cfg.I, torch.bfloat16)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe_layer_amd.moe_layer_forward(x, wg, b, w13, w2, cfg.k, cfg.renorm, bufs=bufs)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe_layer_amd.moe_layer_forward(x, wg, b, w13, w2, cfg.k, cfg.renorm, bufs=bufs)
+    for _ in range(4):
+        bufs.y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gh.from_dev(bufs.y), want)
+        eager = moe_layer_amd.moe_layer_forward(x, wg, b, w13, w2, cfg.k, cfg.renorm)
+        torch.cuda.synchronize()
