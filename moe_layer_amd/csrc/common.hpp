@@ -73,6 +73,11 @@ struct Elem<float> {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// v if ok, else zeros; component-wise, so it stays a register select.
+__device__ __forceinline__ uint4 keep_or_zero(bool ok, uint4 v) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 
 // Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele with shuffles).

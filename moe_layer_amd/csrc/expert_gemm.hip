@@ -1,219 +1,322 @@
-// Expert grouped GEMMs and the gate GEMM (bf16 or fp32 storage, fp32 accumulate).
+// Expert grouped GEMMs (bf16 or fp32 storage, fp32 accumulate):
+//   up   : a[r]      = silu(W1_g x_t) * (W3_g x_t)   from W13_g (2I', H)
+//   down : y_pair[r] = W2_g a[r]                      from W2_g  (H, I')
+// for every sorted pair row r of expert group g (Moebius review, §3.1 gives
+// W13 as (., 2I, H) and W2 as (., H, I); the gate-then-up row order is this
+// library's layout contract).
 //
-// Work unit ("item"): one expert group g and one tile of 16 weight rows.
-//   up   : rows are 8 gate rows (W1, W13 rows [n, n+8)) and the 8 matching up
-//          rows (W3, W13 rows [I'+n, I'+n+8)), so SiLU(gate)*up is formed in
-//          registers (Moebius review §3.1 gives W13 as (., 2I, H); the
-//          gate-then-up row order is this library's layout contract).
-//   down : rows are 16 rows of W2 (., H, I'), i.e. 16 output features.
-//   gate : rows are 16 experts of the gate matrix (E, H) (Sem-MoE notes,
-//          Key design 1: logits = W_g h + b).
-// A block holds the item's weight rows as register-resident K-slabs: wave
-// (ks, ns) keeps fragments [ks*kf, (ks+1)*kf) of n-tile ns, loaded once, and
-// then streams the group's token rows through them 16 at a time.  Each weight
-// byte is read from HBM exactly once per call however many tokens the group
-// has; activations come from L2.  Waves that split K add their partial
-// 16x16 tiles in LDS in a fixed order (no atomics), so results are
-// bit-reproducible.
+// Decode-shaped problems are HBM-bound: every weight byte must stream from
+// HBM exactly once while the token side (a few to a few dozen rows per
+// expert) is small and stays in L2.  The kernel is a set of independent
+// wavefronts; nothing synchronises them after start-up, so a slow load only
+// ever stalls its own wave.  Wave work item = (group g, tile of 16 weight
+// rows, pass of up to 16*NT token rows), over the full K:
+//   up   : the 16 rows are 8 gate rows and the matching 8 up rows, so
+//          SiLU(gate)*up is formed in registers;
+//   down : 16 rows of W2 = 16 output features.
+// K is walked in 512-byte chunks.  Weights are read DRAM-friendly: each load
+// instruction takes 256 contiguous bytes from each of 4 rows (non-temporal,
+// streamed once), double-buffered in registers so chunk c+1 is in flight while
+// chunk c is multiplied.  The wave then passes its 16 rows x 512 B through a
+// private LDS tile (rows padded by 16 B) to read them back in the 16x16 MFMA
+// operand layout (lane l: row l%16, bytes 16*(l/16) of each 64-byte
+// fragment); only the wave itself touches that tile, so no barrier is needed.  Token fragments of chunk c come from
+// L2 just before use and are issued ahead of the next weight chunk, so waiting
+// for them (loads retire in order) never waits for the weights in flight.
+// The stream runs across item boundaries, and the next item's token-row
+// indices are fetched one item ahead.  Token rows past the group's count
+// repeat a real row and are never stored; fragments past the end of K are
+// zero on both sides.  No atomics: every output element is written by exactly
+// one lane, so results are bit-reproducible.
 #include "common.hpp"
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int KF = 16;        // max fragments (x 64 B of K per row) held per wave
-constexpr int BLOCK_MAX = 1024;
+constexpr int XW_WAVES = 4;                             // waves per block (independent)
+constexpr int CHUNK_FRAGS = 8;                          // 64-byte fragments per chunk
+constexpr int CHUNK_BYTES = CHUNK_FRAGS * FRAG_BYTES;   // 512
 
-enum Mode { MODE_UP = 0, MODE_DOWN = 1, MODE_GATE = 2 };
+enum XMode { XMODE_UP = 0, XMODE_DOWN = 1 };
 
-struct GemmArgs {
-  const void* act;         // up/gate: x (T, K); down: A (n_pairs, K)
+struct XArgs {
+  const void* act;         // up: x (T, H); down: a (n_pairs, I')
   const int* sorted_pair;  // up: pair id of each sorted row
-  const int* offsets;      // up/down: (n_groups + 1) row offsets
-  const void* w;           // up: w13 (G, 2I', K); down: w2 (G, H, K); gate: wg (E, K)
-  void* out;               // up: A (n_pairs, I'); down: y_pair (n_pairs, H); gate: logits (T, E)
-  const float* bias;       // gate: (E) or null
+  const int* offsets;      // (n_groups + 1) sorted-row offsets per group
+  const void* w;           // up: w13 (G, 2I', H); down: w2 (G, H, I')
+  void* out;               // up: a (n_pairs, I'); down: y_pair (n_pairs, H)
   int n_groups;
   int kk;
-  int K;                   // contraction length (elements)
-  int I_loc;               // up: I'
-  int n_rows;              // down: H; gate: E (rows of the weight matrix per group)
-  int T;                   // gate: tokens
+  int K;                   // contraction length in elements (up: H, down: I')
+  int I_loc;
+  int H;
   int kfrag_total;         // K * elem / 64
-  int kf;                  // fragments per wave
-  int nw_k;                // waves splitting K
-  int ns;                  // n-tiles per block
-  int n_tiles;             // 16-row tiles per group, grouped by ns: items per group = n_tiles / ns
-  int t_chunk;             // gate: tokens per item
+  int n_tiles;             // 16-row weight tiles per group
 };
 
-template <typename T, int MODE>
-__global__ __launch_bounds__(BLOCK_MAX) void grouped_gemm_kernel(GemmArgs a) {
-  __shared__ int s_list[MAX_GROUPS];
-  __shared__ int s_nlist;
-  __shared__ f32x4_t s_red[MAX_KSPLIT][WAVE];
+// Wave 0: s_off[g] = offsets[g]; s_pstart[g] = number of mp-row passes of the
+// groups before g; s_pstart[n_groups] = total passes.
+__device__ __forceinline__ void pass_prefix(const int* __restrict__ offsets, int n_groups, int mp,
+                                            int* s_pstart, int* s_off) {
+  if (threadIdx.x >= WAVE) return;
+  const int l = lane_id();
+  int base = 0;
+  for (int g0 = 0; g0 <= n_groups; g0 += WAVE) {
+    const int g = g0 + l;
+    if (g <= n_groups) s_off[g] = offsets[g];
+    const int v = (g < n_groups) ? (offsets[g + 1] - offsets[g] + mp - 1) / mp : 0;
+    const int incl = wave_inclusive_scan(v);
+    if (g < n_groups) s_pstart[g] = base + incl - v;
+    base += __shfl(incl, WAVE - 1, WAVE);
+  }
+  if (l == 0) s_pstart[n_groups] = base;
+}
+
+__device__ __forceinline__ uint4 ld16_nt(const char* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int NT>
+struct WItem {
+  int row0, m, t0, n0;     // group's first sorted row, its row count, pass start, first weight row
+  const char* wp[4];       // rows 4j + l/16 (j = 0..3) of the item's 16, + 16*(l%16)
+  int tok[NT];             // activation row of this lane's token in each 16-row tile
+};
+
+template <typename T, int MODE, int NT>
+__device__ __forceinline__ void witem_setup(const XArgs& a, const int* s_pstart, const int* s_off,
+                                            int item, int lrow, int lq, size_t row_bytes,
+                                            WItem<NT>& it) {
+  const int pi = item / a.n_tiles;
+  const int nt = item % a.n_tiles;
+  int lo = 0, hi = a.n_groups;  // s_pstart[lo] <= pi < s_pstart[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pstart[mid] <= pi) lo = mid;
+    else hi = mid;
+  }
+  it.row0 = s_off[lo];
+  it.m = s_off[lo + 1] - it.row0;
+  it.t0 = (pi - s_pstart[lo]) * (16 * NT);
+  // Item row i (0..15) is, for up, gate row n0 + i (i < 8) or up row
+  // I' + n0 + i - 8; for down, W2 row n0 + i.  Rows past the matrix are
+  // clamped (read, never stored).
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * j + lq;
+    size_t wrow;
+    if (MODE == XMODE_UP) {
+      it.n0 = nt * 8;
+      const int n = min(it.n0 + (i & 7), a.I_loc - 1);
+      wrow = static_cast<size_t>(lo) * (2 * a.I_loc) + (i < 8 ? n : a.I_loc + n);
+    } else {
+      it.n0 = nt * 16;
+      wrow = static_cast<size_t>(lo) * a.H + min(it.n0 + i, a.H - 1);
+    }
+    it.wp[j] = reinterpret_cast<const char*>(a.w) + wrow * row_bytes + lrow * 16;
+  }
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int r = it.row0 + min(it.t0 + tt * 16 + lrow, it.m - 1);
+    it.tok[tt] = (MODE == XMODE_UP) ? a.sorted_pair[r] / a.kk : r;
+  }
+}
+
+// Weight bytes of chunk c in the load layout: register i holds row
+// 4*(i%4) + l/16, bytes 256*(i/4) + 16*(l%16) of the chunk (zeros past the
+// end of K).
+__device__ __forceinline__ void wload(const char* const (&wp)[4], int c, int kfrag_total, int lrow,
+                                      uint4 (&w)[CHUNK_FRAGS]) {
+  const int valid = (kfrag_total - c * CHUNK_FRAGS) * FRAG_BYTES;  // valid bytes in this chunk
+  const size_t cb = static_cast<size_t>(c) * CHUNK_BYTES;
+#pragma unroll
+  for (int i = 0; i < CHUNK_FRAGS; ++i) {
+    const int col = 256 * (i / 4) + 16 * lrow;
+    const int colc = col < valid ? col : 0;
+    w[i] = keep_or_zero(col < valid, ld16_nt(wp[i % 4] + cb + (colc - 16 * lrow)));
+  }
+}
+
+// Token fragments of chunk c for every tile (zeros past the end of K).
+template <int NT>
+__device__ __forceinline__ void xload(const char* act, const int (&tok)[NT], size_t row_bytes,
+                                      int lq, int c, int kfrag_total,
+                                      uint4 (&x)[NT][CHUNK_FRAGS]) {
+  const int nf = min(CHUNK_FRAGS, kfrag_total - c * CHUNK_FRAGS);
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const char* p = act + static_cast<size_t>(tok[tt]) * row_bytes + lq * 16 +
+                    static_cast<size_t>(c) * CHUNK_BYTES;
+#pragma unroll
+    for (int f = 0; f < CHUNK_FRAGS; ++f) {
+      x[tt][f] = keep_or_zero(f < nf, ld16(p + min(f, nf - 1) * FRAG_BYTES));
+    }
+  }
+}
+
+constexpr int WT_ROW = CHUNK_BYTES + 16;  // padded row of the wave's LDS tile
+
+// Load layout -> MFMA operand layout through the wave's own LDS tile
+// (16 rows x WT_ROW bytes).  Reads after writes within one wave are ordered.
+__device__ __forceinline__ void wtranspose(const uint4 (&w)[CHUNK_FRAGS], char* tile, int lrow,
+                                           int lq, uint4 (&wt)[CHUNK_FRAGS]) {
+#pragma unroll
+  for (int i = 0; i < CHUNK_FRAGS; ++i)
+    *reinterpret_cast<uint4*>(tile + (4 * (i % 4) + lq) * WT_ROW + 256 * (i / 4) + 16 * lrow) = w[i];
+#pragma unroll
+  for (int f = 0; f < CHUNK_FRAGS; ++f)
+    wt[f] = *reinterpret_cast<const uint4*>(tile + lrow * WT_ROW + FRAG_BYTES * f + 16 * lq);
+}
+
+template <typename T, int NT>
+__device__ __forceinline__ void wmma(const uint4 (&w)[CHUNK_FRAGS], const uint4 (&x)[NT][CHUNK_FRAGS],
+                                     f32x4_t (&acc)[NT]) {
+#pragma unroll
+  for (int f = 0; f < CHUNK_FRAGS; ++f)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = Elem<T>::mma(w[f], x[tt][f], acc[tt]);
+}
+
+// acc[tt][r] = D[4*lq + r][lrow]: weight row 4*lq+r of the item's 16, token row tt*16+lrow.
+template <typename T, int MODE, int NT>
+__device__ __forceinline__ void wstore(const XArgs& a, const WItem<NT>& it, f32x4_t (&acc)[NT],
+                                       int lrow, int lq) {
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int tr = it.t0 + tt * 16 + lrow;
+    if (MODE == XMODE_UP) {
+      float up[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) up[r] = __shfl_xor(acc[tt][r], 32, WAVE);
+      const int n = it.n0 + 4 * lq;
+      if (lq < 2 && tr < it.m && n < a.I_loc) {
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gt = acc[tt][r];
+          o[r] = gt / (1.0f + __expf(-gt)) * up[r];
+        }
+        T* dst = reinterpret_cast<T*>(a.out) + static_cast<size_t>(it.row0 + tr) * a.I_loc + n;
+        Elem<T>::store4(dst, o[0], o[1], o[2], o[3]);
+      }
+    } else {
+      const int n = it.n0 + 4 * lq;
+      if (tr < it.m && n < a.H) {
+        T* dst = reinterpret_cast<T*>(a.out) + static_cast<size_t>(it.row0 + tr) * a.H + n;
+        Elem<T>::store4(dst, acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
+      }
+    }
+    acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+template <typename T, int MODE, int NT>
+__global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
+  __shared__ int s_pstart[MAX_GROUPS + 1];
+  __shared__ int s_off[MAX_GROUPS + 1];
+  __shared__ __attribute__((aligned(16))) char s_wt[XW_WAVES][16 * WT_ROW];
 
   const int wv = threadIdx.x / WAVE;
-  const int ks = wv % a.nw_k;
-  const int nsi = wv / a.nw_k;
   const int l = lane_id();
   const int lrow = l & 15;
   const int lq = l >> 4;
-  const int items_per_group = a.n_tiles / a.ns;
 
-  int n_items;
-  if (MODE == MODE_GATE) {
-    n_items = items_per_group * ((a.T + a.t_chunk - 1) / a.t_chunk);
-  } else {
-    touched_groups(a.offsets, a.n_groups, s_list, &s_nlist);
-    __syncthreads();
-    n_items = s_nlist * items_per_group;
-  }
+  pass_prefix(a.offsets, a.n_groups, 16 * NT, s_pstart, s_off);
+  __syncthreads();  // the only barrier; waves are independent from here on
+  const int total = s_pstart[a.n_groups] * a.n_tiles;
+  const int stride = gridDim.x * XW_WAVES;
+  int item = blockIdx.x * XW_WAVES + wv;
+  if (item >= total) return;  // wave-uniform
 
-  const int f0 = ks * a.kf;
-  const int nf = min(a.kf, a.kfrag_total - f0);
   const size_t row_bytes = static_cast<size_t>(a.K) * sizeof(T);
-  const char* wbase = reinterpret_cast<const char*>(a.w);
-  const char* abase = reinterpret_cast<const char*>(a.act);
+  const int nck = (a.kfrag_total + CHUNK_FRAGS - 1) / CHUNK_FRAGS;
+  const char* act = reinterpret_cast<const char*>(a.act);
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int gi = item / items_per_group;
-    const int nt = (item % items_per_group) * a.ns + nsi;
-    int g = 0, row0 = 0, m = 0;
-    if (MODE == MODE_GATE) {
-      row0 = gi * a.t_chunk;
-      m = min(a.t_chunk, a.T - row0);
-    } else {
-      g = s_list[gi];
-      row0 = a.offsets[g];
-      m = a.offsets[g + 1] - row0;
-    }
+  WItem<NT> cur, nxt;
+  witem_setup<T, MODE, NT>(a, s_pstart, s_off, item, lrow, lq, row_bytes, cur);
+  bool have_nxt = item + stride < total;
+  if (have_nxt) witem_setup<T, MODE, NT>(a, s_pstart, s_off, item + stride, lrow, lq, row_bytes, nxt);
 
-    // This lane's weight row.
-    size_t wrow;
-    if (MODE == MODE_UP) {
-      const int r = (lrow < 8) ? (nt * 8 + lrow) : (a.I_loc + nt * 8 + (lrow - 8));
-      wrow = static_cast<size_t>(g) * (2 * a.I_loc) + r;
-    } else if (MODE == MODE_DOWN) {
-      wrow = static_cast<size_t>(g) * a.n_rows + nt * 16 + lrow;
-    } else {
-      wrow = min(nt * 16 + lrow, a.n_rows - 1);
-    }
-    const char* wp = wbase + wrow * row_bytes + static_cast<size_t>(f0) * FRAG_BYTES + lq * 16;
-    uint4 wf[KF];
+  f32x4_t acc[NT];
 #pragma unroll
-    for (int f = 0; f < KF; ++f)
-      if (f < nf) wf[f] = ld16(wp + f * FRAG_BYTES);
+  for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 w0[CHUNK_FRAGS], w1[CHUNK_FRAGS], x[NT][CHUNK_FRAGS];
+  char* tile = s_wt[wv];
+  wload(cur.wp, 0, a.kfrag_total, lrow, w0);
+  int c = 0;
 
-    for (int mt = 0; mt < m; mt += 16) {
-      const int r_in = mt + lrow;
-      const int r_cl = (r_in < m) ? r_in : (m - 1);  // padded rows repeat a real row, never stored
-      size_t arow;
-      if (MODE == MODE_UP) arow = static_cast<size_t>(a.sorted_pair[row0 + r_cl] / a.kk);
-      else arow = static_cast<size_t>(row0 + r_cl);
-      const char* ap = abase + arow * row_bytes + static_cast<size_t>(f0) * FRAG_BYTES + lq * 16;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int f = 0; f < KF; ++f)
-        if (f < nf) acc = Elem<T>::mma(wf[f], ld16(ap + f * FRAG_BYTES), acc);
-
-      bool owner = true;
-      if (a.nw_k > 1) {
-        s_red[wv][l] = acc;
-        __syncthreads();
-        owner = (ks == 0);
-        if (owner) {
-          for (int v = 1; v < a.nw_k; ++v) acc += s_red[wv + v][l];
-        }
-        __syncthreads();
-      }
-      if (!owner) continue;
-
-      // acc[r] = D[4*lq + r][lrow]: weight row 4*lq+r of the tile, token row lrow.
-      const bool valid = r_in < m;
-      if (MODE == MODE_UP) {
-        float up[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) up[r] = __shfl_xor(acc[r], 32, WAVE);
-        if (lq < 2 && valid) {
-          float o[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float gt = acc[r];
-            o[r] = gt / (1.0f + __expf(-gt)) * up[r];
-          }
-          T* dst = reinterpret_cast<T*>(a.out) + static_cast<size_t>(row0 + r_in) * a.I_loc + nt * 8 + 4 * lq;
-          Elem<T>::store4(dst, o[0], o[1], o[2], o[3]);
-        }
-      } else if (MODE == MODE_DOWN) {
-        if (valid) {
-          T* dst = reinterpret_cast<T*>(a.out) + static_cast<size_t>(row0 + r_in) * a.n_rows + nt * 16 + 4 * lq;
-          Elem<T>::store4(dst, acc[0], acc[1], acc[2], acc[3]);
-        }
-      } else {
-        if (valid) {
-          float* dst = reinterpret_cast<float*>(a.out) + static_cast<size_t>(row0 + r_in) * a.n_rows;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = nt * 16 + 4 * lq + r;
-            if (e < a.n_rows) dst[e] = acc[r] + (a.bias ? a.bias[e] : 0.f);
-          }
-        }
-      }
-    }
+  // One step: token fragments of (cur, c); weights of the next chunk into WN;
+  // multiply WC; at the end of an item store it and move on (break when the
+  // wave has no more work).
+#define XSTEP(WC, WN)                                                                     \
+  {                                                                                       \
+    xload<NT>(act, cur.tok, row_bytes, lq, c, a.kfrag_total, x);                          \
+    const bool last = c + 1 >= nck;                                                       \
+    if (!last) wload(cur.wp, c + 1, a.kfrag_total, lrow, WN);                             \
+    else if (have_nxt) wload(nxt.wp, 0, a.kfrag_total, lrow, WN);                         \
+    {                                                                                     \
+      uint4 wt[CHUNK_FRAGS];                                                              \
+      wtranspose(WC, tile, lrow, lq, wt);                                                 \
+      wmma<T, NT>(wt, x, acc);                                                            \
+    }                                                                                     \
+    if (!last) {                                                                          \
+      ++c;                                                                                \
+    } else {                                                                              \
+      wstore<T, MODE, NT>(a, cur, acc, lrow, lq);                                         \
+      if (!have_nxt) break;                                                               \
+      item += stride;                                                                     \
+      cur = nxt;                                                                          \
+      c = 0;                                                                              \
+      have_nxt = item + stride < total;                                                   \
+      if (have_nxt)                                                                       \
+        witem_setup<T, MODE, NT>(a, s_pstart, s_off, item + stride, lrow, lq, row_bytes, nxt); \
+    }                                                                                     \
   }
+
+  while (true) {
+    XSTEP(w0, w1)
+    XSTEP(w1, w0)
+  }
+#undef XSTEP
 }
 
 // ---------------------------------------------------------------- host side
 
-static int g_cu_count[64];
+static int elem_bytes_x(int dtype) { return dtype == 1 ? 2 : 4; }
 
-int device_cu_count() {
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  if (dev < 0 || dev >= 64) dev = 0;
-  if (g_cu_count[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    g_cu_count[dev] = n;
-  }
-  return g_cu_count[dev];
+// Token rows per pass (16 * NT) from the mean rows per group (exact for the
+// full and TP views; an over-estimate for an EP share).
+static int pick_nt(int T, int kk, int n_groups) {
+  const double mean = static_cast<double>(T) * kk / n_groups;
+  return (mean > 12.0 && T > 16) ? 2 : 1;
 }
 
-// Split K into nw_k waves of at most KF fragments each.
-static void split_k(GemmArgs& a) {
-  a.nw_k = (a.kfrag_total + KF - 1) / KF;
-  a.kf = (a.kfrag_total + a.nw_k - 1) / a.nw_k;
-  a.nw_k = (a.kfrag_total + a.kf - 1) / a.kf;
-}
-
-// Largest divisor of n_tiles that keeps the block at or under `max_waves` waves.
-static int pick_ns(int n_tiles, int nw_k, int max_waves) {
-  int best = 1;
-  for (int d = 1; d <= n_tiles && d * nw_k <= max_waves; ++d)
-    if (n_tiles % d == 0) best = d;
-  return best;
+template <int MODE, int NT>
+static void launch_x(int dtype, const XArgs& a, int T, int kk, hipStream_t s) {
+  const long long pairs = static_cast<long long>(T) * kk;
+  const long long touched = a.n_groups < pairs ? a.n_groups : pairs;
+  const long long max_items = (pairs / (16 * NT) + touched) * a.n_tiles;
+  long long grid = (max_items + XW_WAVES - 1) / XW_WAVES;
+  const long long cap = static_cast<long long>(device_cu_count()) * 8;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  if (dtype == 1)
+    hipLaunchKernelGGL((expert_wave_kernel<uint16_t, MODE, NT>), dim3(grid), dim3(XW_WAVES * WAVE), 0, s, a);
+  else
+    hipLaunchKernelGGL((expert_wave_kernel<float, MODE, NT>), dim3(grid), dim3(XW_WAVES * WAVE), 0, s, a);
 }
 
 template <int MODE>
-static void launch(int dtype, GemmArgs a, int max_items, hipStream_t s) {
-  const int threads = a.nw_k * a.ns * WAVE;
-  const int per_cu = (BLOCK_MAX * 2) / threads;  // aim for ~32 resident waves per CU
-  int grid = device_cu_count() * (per_cu > 0 ? per_cu : 1);
-  if (grid > max_items) grid = max_items;
-  if (grid < 1) grid = 1;
-  if (dtype == 1)
-    hipLaunchKernelGGL((grouped_gemm_kernel<uint16_t, MODE>), dim3(grid), dim3(threads), 0, s, a);
-  else
-    hipLaunchKernelGGL((grouped_gemm_kernel<float, MODE>), dim3(grid), dim3(threads), 0, s, a);
+static void launch_mode(int dtype, const XArgs& a, int T, int kk, hipStream_t s) {
+  if (pick_nt(T, kk, a.n_groups) == 1) launch_x<MODE, 1>(dtype, a, T, kk, s);
+  else launch_x<MODE, 2>(dtype, a, T, kk, s);
 }
-
-static int elem_bytes(int dtype) { return dtype == 1 ? 2 : 4; }
 
 void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, const int32_t* offsets,
                       int n_groups, int T, int kk, const void* w13, int H, int I, void* A,
                       hipStream_t s) {
-  GemmArgs a{};
+  XArgs a{};
   a.act = x;
   a.sorted_pair = sorted_pair;
   a.offsets = offsets;
@@ -223,17 +326,15 @@ void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, cons
   a.kk = kk;
   a.K = H;
   a.I_loc = I;
-  a.kfrag_total = H * elem_bytes(dtype) / FRAG_BYTES;
-  split_k(a);
-  a.n_tiles = I / 8;
-  a.ns = pick_ns(a.n_tiles, a.nw_k, 8);
-  const int touched_max = n_groups < T * kk ? n_groups : T * kk;
-  launch<MODE_UP>(dtype, a, touched_max * (a.n_tiles / a.ns), s);
+  a.H = H;
+  a.kfrag_total = H * elem_bytes_x(dtype) / FRAG_BYTES;
+  a.n_tiles = (I + 7) / 8;
+  launch_mode<XMODE_UP>(dtype, a, T, kk, s);
 }
 
 void launch_expert_down(int dtype, const void* A, const int32_t* offsets, int n_groups, int T,
                         int kk, const void* w2, int H, int I, void* y_pair, hipStream_t s) {
-  GemmArgs a{};
+  XArgs a{};
   a.act = A;
   a.offsets = offsets;
   a.w = w2;
@@ -241,38 +342,11 @@ void launch_expert_down(int dtype, const void* A, const int32_t* offsets, int n_
   a.n_groups = n_groups;
   a.kk = kk;
   a.K = I;
-  a.n_rows = H;
-  a.kfrag_total = I * elem_bytes(dtype) / FRAG_BYTES;
-  split_k(a);
-  a.n_tiles = H / 16;
-  a.ns = pick_ns(a.n_tiles, a.nw_k, 8);
-  const int touched_max = n_groups < T * kk ? n_groups : T * kk;
-  launch<MODE_DOWN>(dtype, a, touched_max * (a.n_tiles / a.ns), s);
-}
-
-void launch_gate_gemm(int dtype, const void* x, const void* wg, const float* bias, float* logits,
-                      int T, int H, int E, hipStream_t s) {
-  GemmArgs a{};
-  a.act = x;
-  a.w = wg;
-  a.out = logits;
-  a.bias = bias;
-  a.K = H;
-  a.n_rows = E;
-  a.T = T;
-  a.kfrag_total = H * elem_bytes(dtype) / FRAG_BYTES;
-  split_k(a);
-  a.n_tiles = (E + 15) / 16;
-  a.ns = 1;
-  // Enough items to spread the gate matrix and the tokens over the chip.
-  const int want_items = 2 * device_cu_count();
-  int chunks = (want_items + a.n_tiles - 1) / a.n_tiles;
-  int t_chunk = (T + chunks - 1) / chunks;
-  t_chunk = ((t_chunk + 15) / 16) * 16;
-  if (t_chunk < 16) t_chunk = 16;
-  a.t_chunk = t_chunk;
-  const int n_items = a.n_tiles * ((T + t_chunk - 1) / t_chunk);
-  launch<MODE_GATE>(dtype, a, n_items, s);
+  a.I_loc = I;
+  a.H = H;
+  a.kfrag_total = I * elem_bytes_x(dtype) / FRAG_BYTES;
+  a.n_tiles = (H + 15) / 16;
+  launch_mode<XMODE_DOWN>(dtype, a, T, kk, s);
 }
 
 }  // namespace moe
