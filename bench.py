@@ -4,8 +4,9 @@ the dominant kernel and the CPU oracle timed beside it.
     python bench.py [--steps K] [--warmup W] [--workload NAME --tokens T --routing R]
     python bench.py --sweep --out results.jsonl     # every batch of the EP/TP/30B workloads
 
-A step is one pass of the whole hot path (gate GEMM + softmax/top-k, permute,
-expert up-projection with SiLU*up, down-projection, combine) over one batch
+A step is one pass of the whole hot path (gate GEMM + softmax/top-k + permute
+in one launch, expert up-projection with SiLU*up, down-projection, combine:
+four launches) over one batch
 of seeded synthetic input already resident in HBM.  Weights are rotated over
 enough bit-identical copies (>= 1 GB in total) that the 256 MB Infinity
 Cache cannot serve them.  Prints ONE JSON line (rank 0; this build runs on
@@ -28,6 +29,45 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 1.0e9
 DEFAULT = ("dsv2_lite", 256, "uniform")
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "expert_up_counters.json")
+
+
+def bench_repack(steps, warmup):
+    """EP->TP local permute of one Qwen3-235B-shaped EP rank (16 experts, P=8):
+    a pure copy of 604 MB read + 604 MB written."""
+    import torch
+
+    import moe_layer_amd
+    from moe_inputs import get_config, make_repack_inputs
+    cfg = get_config("qwen3_235b_tp")
+    r = make_repack_inputs(cfg, rank=0)
+    import numpy as np
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    w13, w2 = dev(r["w13_ep"]), dev(r["w2_ep"])
+    P, E_l, Ip = cfg.P, cfg.E // cfg.P, cfg.I // cfg.P
+    d13 = [torch.empty((E_l, 2 * Ip, cfg.H), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    d2 = [torch.empty((E_l, cfg.H, Ip), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    for _ in range(warmup):
+        moe_layer_amd.moe_repack_ep_to_tp(w13, w2, P, d13, d2)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        moe_layer_amd.moe_repack_ep_to_tp(w13, w2, P, d13, d2)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / steps * 1e-3
+    moved = 2 * (w13.numel() + w2.numel()) * 2
+    gbs = moved / t / 1e9
+    return {
+        "metric": "EP->TP expert-weight repack throughput (read + write)",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": t * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "repack 16 EP experts of Qwen3-235B-A22B shape into 8 TP blocks",
+                   "bytes_read": moved // 2, "bytes_written": moved // 2},
+        "roofline": {"bound": "hbm", "kernel": "repack", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+    }
 
 
 def parse():
@@ -105,16 +145,16 @@ def run_step(wl, i, events=None):
     w13, w2 = wl.w13[i % wl.copies], wl.w2[i % wl.copies]
     ev = events
     if ev: ev[0].record()
-    m.moe_route(wl.x, wl.w_gate, wl.bias, c.k, c.renorm, c.n_shared, b.logits, b.topk_ids, b.topk_w)
+    m.moe_route_permute(wl.x, wl.w_gate, wl.bias, c.k, c.renorm, c.n_shared, b.logits, b.topk_ids,
+                        b.topk_w, wl.g_begin, c.n_groups, b.counts, b.offsets, b.sorted_pair,
+                        b.pair_pos, b.route_ws)
     if ev: ev[1].record()
-    m.moe_permute(b.topk_ids, wl.g_begin, c.n_groups, b.counts, b.offsets, b.sorted_pair, b.pair_pos)
-    if ev: ev[2].record()
     m.moe_expert_up(wl.x, b.sorted_pair, b.offsets, c.kk, w13, b.a)
-    if ev: ev[3].record()
+    if ev: ev[2].record()
     m.moe_expert_down(b.a, b.offsets, wl.T, c.kk, w2, b.y_pair)
-    if ev: ev[4].record()
+    if ev: ev[3].record()
     m.moe_combine(b.y_pair, b.pair_pos, b.topk_w, b.y)
-    if ev: ev[5].record()
+    if ev: ev[4].record()
 
 
 def algorithmic(wl):
@@ -145,12 +185,12 @@ def time_workload(wl, steps, warmup, graph=False):
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / steps
     # per-kernel durations from events recorded on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         run_step(wl, i, evs[i])
     torch.cuda.synchronize()
-    names = ("route", "permute", "expert_up", "expert_down", "combine")
+    names = ("route_permute", "expert_up", "expert_down", "combine")
     per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps * 1e3
            for j, n in enumerate(names)}
     out = {"t_step_s": t_step, "kernels_us": per}
@@ -297,6 +337,10 @@ def main():
                         out.flush()
                     del wl
                     torch.cuda.empty_cache()
+        return
+
+    if args.workload == "repack":
+        print(json.dumps(bench_repack(args.steps, args.warmup)), flush=True)
         return
 
     name = args.workload

@@ -59,14 +59,22 @@ int moe_abi_version(void);
 /* Human-readable text for a status code (static storage). */
 const char* moe_status_str(int status);
 
-/* Workspace bytes `op` needs for these sizes (0 if none).  Only
- * MOE_OP_GROUPED_GEMM uses a workspace: the (T*kk, I) intermediate
- * activations silu(W1 x) * W3 x in the storage dtype. */
+/* Workspace bytes `op` needs for these sizes (0 if none).  For
+ * MOE_OP_GROUPED_GEMM: the (T*kk, I) intermediate activations
+ * silu(W1 x) * W3 x in the storage dtype.  (Routing: moe_route_workspace_bytes.) */
 size_t moe_workspace_bytes(int op, int T, int kk, int n_groups, int H, int I, int dtype);
 
+/* Workspace bytes moe_route and moe_route_permute need for T tokens, hidden
+ * size H and E routed experts (per-token-tile counters, then K-slice partial
+ * logits).  The buffer must be zero-filled before its first use; every
+ * completed call leaves its counter head zero again, so the same buffer can
+ * be reused call after call.  Calls sharing one buffer must be ordered (one
+ * stream, or synchronised streams). */
+size_t moe_route_workspace_bytes(int T, int H, int E, int dtype);
+
 /*
- * moe_route -- gate GEMM, softmax and top-k (Sem-MoE notes, Key design 1:
- * G(h) = top-k(softmax(W_g h + b_g))).
+ * moe_route -- gate GEMM, softmax and top-k in one launch (Sem-MoE notes,
+ * Key design 1: G(h) = top-k(softmax(W_g h + b_g))).
  *   x          (T, H) dtype          token activations
  *   w_gate     (E, H) dtype          gate matrix
  *   gate_bias  (E) fp32, nullable    added to the logits before softmax and top-k
@@ -76,12 +84,25 @@ size_t moe_workspace_bytes(int op, int T, int kk, int n_groups, int H, int I, in
  *   topk_w     (T, k + n_shared) fp32 [out]   softmax over all E routed experts
  *              at the picked ids; if renorm != 0, divided by their sum over the
  *              k picks; shared slots weigh 1.
+ *   ws         >= moe_route_workspace_bytes(T, H, E, dtype) bytes (see above)
  * Limits: 1 <= E <= 512; 1 <= k <= min(E, 32); k + n_shared <= 64;
- * H * sizeof(dtype) a multiple of 64 and at most 16384 bytes (MOE_EUNSUPPORTED).
+ * H * sizeof(dtype) a multiple of 64 (MOE_EUNSUPPORTED).
  */
 int moe_route(const void* x, const void* w_gate, const float* gate_bias, int T, int H, int E, int k,
               int renorm, int n_shared, int dtype, float* logits, int32_t* topk_ids, float* topk_w,
-              hipStream_t stream);
+              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_route_permute -- moe_route followed by moe_permute of its ids, in one
+ * launch (the last block to finish the routing sorts the pairs).  Arguments
+ * and outputs are those of the two calls; the same workspace rules as
+ * moe_route apply.
+ */
+int moe_route_permute(const void* x, const void* w_gate, const float* gate_bias, int T, int H, int E,
+                      int k, int renorm, int n_shared, int dtype, float* logits, int32_t* topk_ids,
+                      float* topk_w, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,
+                      int32_t* sorted_pair, int32_t* pair_pos, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
 
 /*
  * moe_permute -- expert counts, offsets and the stable argsort of the
@@ -113,8 +134,8 @@ int moe_permute(const int32_t* topk_ids, int T, int kk, int g_begin, int n_group
  *   w2          (n_groups, H, I) dtype
  *   y_pair      (T*kk, H) dtype [out]     first n_kept rows written
  *   ws          >= moe_workspace_bytes(MOE_OP_GROUPED_GEMM, ...) bytes, holds a
- * Limits: H * sizeof(dtype) a multiple of 64 and <= 16384 bytes; H % 16 == 0;
- * I * sizeof(dtype) a multiple of 64 and <= 16384 bytes; n_groups <= 512.
+ * Limits: H * sizeof(dtype) and I * sizeof(dtype) multiples of 64; H % 16 == 0;
+ * I % 8 == 0; n_groups <= 512.
  * a is rounded to dtype before the W2 product.
  */
 int moe_grouped_gemm(const void* x, const int32_t* sorted_pair, const int32_t* offsets, int T, int kk,

@@ -19,8 +19,9 @@ MOE_DTYPE_BF16 = 1
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM, MOE_OP_COMBINE, MOE_OP_REPACK = range(5)
 
 EXPORTED = (
-    "moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
-    "moe_grouped_gemm", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_repack_ep_to_tp",
+    "moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes",
+    "moe_route", "moe_route_permute", "moe_permute", "moe_grouped_gemm", "moe_expert_up",
+    "moe_expert_down", "moe_combine", "moe_repack_ep_to_tp",
 )
 
 
@@ -52,8 +53,13 @@ def lib():
     L.moe_status_str.argtypes = [_i]
     L.moe_workspace_bytes.restype = _sz
     L.moe_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+    L.moe_route_workspace_bytes.restype = _sz
+    L.moe_route_workspace_bytes.argtypes = [_i, _i, _i, _i]
     L.moe_route.restype = _i
-    L.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p]
+    L.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]
+    L.moe_route_permute.restype = _i
+    L.moe_route_permute.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i,
+                                    _p, _p, _p, _p, _p, _sz, _p]
     L.moe_permute.restype = _i
     L.moe_permute.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p]
     L.moe_grouped_gemm.restype = _i
@@ -113,18 +119,49 @@ def moe_workspace_bytes(op, T, kk, n_groups, H, I, dtype_code):
     return lib().moe_workspace_bytes(op, T, kk, n_groups, H, I, dtype_code)
 
 
-def moe_route(x, w_gate, gate_bias, k, renorm, n_shared, logits, topk_ids, topk_w, stream=None):
+def moe_route_workspace_bytes(T, H, E, dtype_code):
+    return lib().moe_route_workspace_bytes(T, H, E, dtype_code)
+
+
+def route_workspace(T, H, E, dtype, device="cuda"):
+    """A zero-filled routing workspace (reusable: every call leaves it zeroed)."""
+    code = MOE_DTYPE_BF16 if dtype == torch.bfloat16 else MOE_DTYPE_F32
+    n = max(moe_route_workspace_bytes(T, H, E, code), 256)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def _route_common(x, w_gate, gate_bias, k, n_shared, logits, topk_ids, topk_w):
     T, H = x.shape
     E = w_gate.shape[0]
     kk = k + n_shared
-    dt = _dtype_code(x)
-    st = lib().moe_route(
-        _ptr(x, "x"), _ptr(w_gate, "w_gate", x.dtype, (E, H)),
-        _ptr(gate_bias, "gate_bias", torch.float32, (E,)), T, H, E, k, int(bool(renorm)), n_shared,
-        dt, _ptr(logits, "logits", torch.float32, (T, E)),
-        _ptr(topk_ids, "topk_ids", torch.int32, (T, kk)),
-        _ptr(topk_w, "topk_w", torch.float32, (T, kk)), _stream(stream))
+    return (_ptr(x, "x"), _ptr(w_gate, "w_gate", x.dtype, (E, H)),
+            _ptr(gate_bias, "gate_bias", torch.float32, (E,)), T, H, E,
+            _ptr(logits, "logits", torch.float32, (T, E)),
+            _ptr(topk_ids, "topk_ids", torch.int32, (T, kk)),
+            _ptr(topk_w, "topk_w", torch.float32, (T, kk)))
+
+
+def moe_route(x, w_gate, gate_bias, k, renorm, n_shared, logits, topk_ids, topk_w, ws, stream=None):
+    px, pw, pb, T, H, E, pl, pi, pww = _route_common(x, w_gate, gate_bias, k, n_shared, logits,
+                                                     topk_ids, topk_w)
+    st = lib().moe_route(px, pw, pb, T, H, E, k, int(bool(renorm)), n_shared, _dtype_code(x), pl, pi,
+                         pww, _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check("moe_route", st)
+
+
+def moe_route_permute(x, w_gate, gate_bias, k, renorm, n_shared, logits, topk_ids, topk_w,
+                      g_begin, n_groups, counts, offsets, sorted_pair, pair_pos, ws, stream=None):
+    px, pw, pb, T, H, E, pl, pi, pww = _route_common(x, w_gate, gate_bias, k, n_shared, logits,
+                                                     topk_ids, topk_w)
+    kk = k + n_shared
+    st = lib().moe_route_permute(
+        px, pw, pb, T, H, E, k, int(bool(renorm)), n_shared, _dtype_code(x), pl, pi, pww, g_begin,
+        n_groups, _ptr(counts, "counts", torch.int32, (n_groups,)),
+        _ptr(offsets, "offsets", torch.int32, (n_groups + 1,)),
+        _ptr(sorted_pair, "sorted_pair", torch.int32, (T * kk,)),
+        _ptr(pair_pos, "pair_pos", torch.int32, (T * kk,)), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream))
+    _check("moe_route_permute", st)
 
 
 def moe_permute(topk_ids, g_begin, n_groups, counts, offsets, sorted_pair, pair_pos, stream=None):

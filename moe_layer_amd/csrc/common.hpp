@@ -78,6 +78,38 @@ __device__ __forceinline__ uint4 keep_or_zero(bool ok, uint4 v) {
   return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
 }
 
+// Relaxed loads and stores at agent scope (global_load/store with sc1): they
+// are coherent across the XCDs' separate L2 caches on their own, so data handed
+// from one block to another inside a launch needs no whole-cache write-back or
+// invalidate, only these accesses and a wait for the stores to complete.
+template <typename V>
+__device__ __forceinline__ V ld_agent(const V* p) {
+  return __hip_atomic_load(const_cast<V*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ void st_agent(V* p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival counter shared by the blocks of one launch: returns true, in every
+// thread of the block, for the block that arrives n-th at *ctr, and that block
+// resets the counter to zero.  Everything the arriving blocks stored with
+// st_agent before the call is visible to ld_agent loads of the last block
+// after it: each wave waits for its own stores to complete (vmcnt counts
+// stores on gfx9) before the block barrier that precedes the atomic.
+__device__ __forceinline__ bool last_to_arrive(int* ctr, int n, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = atomicAdd(ctr, 1);
+    const int last = old == n - 1;
+    if (last) st_agent(ctr, 0);
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 
 // Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele with shuffles).

@@ -124,8 +124,10 @@ __device__ __forceinline__ void witem_setup(const XArgs& a, const int* s_pstart,
 }
 
 // Weight bytes of chunk c in the load layout: register i holds row
-// 4*(i%4) + l/16, bytes 256*(i/4) + 16*(l%16) of the chunk (zeros past the
-// end of K).
+// 4*(i%4) + l/16, bytes 256*(i/4) + 16*(l%16) of the chunk.  Past the end of
+// K (partial last chunk) the lane re-reads the chunk's first bytes: finite
+// data that meets zero token fragments.  The loaded registers are never
+// touched until use, so the loads stay in flight.
 __device__ __forceinline__ void wload(const char* const (&wp)[4], int c, int kfrag_total, int lrow,
                                       uint4 (&w)[CHUNK_FRAGS]) {
   const int valid = (kfrag_total - c * CHUNK_FRAGS) * FRAG_BYTES;  // valid bytes in this chunk
@@ -134,11 +136,12 @@ __device__ __forceinline__ void wload(const char* const (&wp)[4], int c, int kfr
   for (int i = 0; i < CHUNK_FRAGS; ++i) {
     const int col = 256 * (i / 4) + 16 * lrow;
     const int colc = col < valid ? col : 0;
-    w[i] = keep_or_zero(col < valid, ld16_nt(wp[i % 4] + cb + (colc - 16 * lrow)));
+    w[i] = ld16_nt(wp[i % 4] + cb + (colc - 16 * lrow));
   }
 }
 
-// Token fragments of chunk c for every tile (zeros past the end of K).
+// Token fragments of chunk c for every tile (past the end of K the lane
+// re-reads a valid fragment; wmma() zeroes those at use).
 template <int NT>
 __device__ __forceinline__ void xload(const char* act, const int (&tok)[NT], size_t row_bytes,
                                       int lq, int c, int kfrag_total,
@@ -150,7 +153,7 @@ __device__ __forceinline__ void xload(const char* act, const int (&tok)[NT], siz
                     static_cast<size_t>(c) * CHUNK_BYTES;
 #pragma unroll
     for (int f = 0; f < CHUNK_FRAGS; ++f) {
-      x[tt][f] = keep_or_zero(f < nf, ld16(p + min(f, nf - 1) * FRAG_BYTES));
+      x[tt][f] = ld16(p + min(f, nf - 1) * FRAG_BYTES);
     }
   }
 }
@@ -169,13 +172,15 @@ __device__ __forceinline__ void wtranspose(const uint4 (&w)[CHUNK_FRAGS], char* 
     wt[f] = *reinterpret_cast<const uint4*>(tile + lrow * WT_ROW + FRAG_BYTES * f + 16 * lq);
 }
 
+// Fragments f >= nf lie past the end of K: their token side is zeroed here,
+// so they add exactly nothing whatever the weight side holds.
 template <typename T, int NT>
 __device__ __forceinline__ void wmma(const uint4 (&w)[CHUNK_FRAGS], const uint4 (&x)[NT][CHUNK_FRAGS],
-                                     f32x4_t (&acc)[NT]) {
+                                     int nf, f32x4_t (&acc)[NT]) {
 #pragma unroll
   for (int f = 0; f < CHUNK_FRAGS; ++f)
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) acc[tt] = Elem<T>::mma(w[f], x[tt][f], acc[tt]);
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = Elem<T>::mma(w[f], keep_or_zero(f < nf, x[tt][f]), acc[tt]);
 }
 
 // acc[tt][r] = D[4*lq + r][lrow]: weight row 4*lq+r of the item's 16, token row tt*16+lrow.
@@ -252,13 +257,22 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
 #define XSTEP(WC, WN)                                                                     \
   {                                                                                       \
     xload<NT>(act, cur.tok, row_bytes, lq, c, a.kfrag_total, x);                          \
+    __builtin_amdgcn_sched_barrier(0); /* token loads stay ahead of the weight loads */   \
     const bool last = c + 1 >= nck;                                                       \
-    if (!last) wload(cur.wp, c + 1, a.kfrag_total, lrow, WN);                             \
-    else if (have_nxt) wload(nxt.wp, 0, a.kfrag_total, lrow, WN);                         \
+    /* One weight load on every path (next chunk, next item's first chunk, or with no  */ \
+    /* work left a harmless re-read of this chunk), so the same number of loads is     */ \
+    /* outstanding whichever way the step went and no wait drains the prefetch.        */ \
+    {                                                                                     \
+      const bool to_next = last && have_nxt;                                              \
+      const char* np[4];                                                                  \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) np[j] = to_next ? nxt.wp[j] : cur.wp[j]; \
+      wload(np, last ? (have_nxt ? 0 : c) : c + 1, a.kfrag_total, lrow, WN);              \
+    }                                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
     {                                                                                     \
       uint4 wt[CHUNK_FRAGS];                                                              \
       wtranspose(WC, tile, lrow, lq, wt);                                                 \
-      wmma<T, NT>(wt, x, acc);                                                            \
+      wmma<T, NT>(wt, x, min(CHUNK_FRAGS, a.kfrag_total - c * CHUNK_FRAGS), acc);           \
     }                                                                                     \
     if (!last) {                                                                          \
       ++c;                                                                                \

@@ -3,22 +3,40 @@
 #include "moe.h"
 #include "moe_internal.h"
 
+namespace moe {
+
+static int g_cu_count[64];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_cu_count[dev] = n;
+  }
+  return g_cu_count[dev];
+}
+
+}  // namespace moe
+
 using namespace moe;
 
 namespace {
 
-constexpr int ABI_VERSION = 1;
+constexpr int ABI_VERSION = 2;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 int elem_bytes(int dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
 bool dtype_ok(int dtype) { return dtype == MOE_DTYPE_F32 || dtype == MOE_DTYPE_BF16; }
 
-// A contraction length the fragment kernels take: whole 64-byte K-chunks,
-// at most MAX_KSPLIT waves of 16 chunks.
+// A contraction length the fragment kernels take: whole 64-byte K fragments
+// (rows of at most 1 MiB).
 bool k_len_ok(int K, int dtype) {
   const long long b = static_cast<long long>(K) * elem_bytes(dtype);
-  return b % 64 == 0 && b <= 64LL * 16 * MAX_KSPLIT;
+  return b % 64 == 0 && b <= (1LL << 20);
 }
 
 int launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP; }
@@ -58,9 +76,16 @@ size_t moe_workspace_bytes(int op, int T, int kk, int n_groups, int H, int I, in
   return (b + 255) & ~static_cast<size_t>(255);
 }
 
-int moe_route(const void* x, const void* w_gate, const float* gate_bias, int T, int H, int E, int k,
-              int renorm, int n_shared, int dtype, float* logits, int32_t* topk_ids, float* topk_w,
-              hipStream_t stream) {
+size_t moe_route_workspace_bytes(int T, int H, int E, int dtype) {
+  if (T <= 0 || H <= 0 || E <= 0 || !dtype_ok(dtype)) return 0;
+  return route_workspace_bytes(T, H, E, dtype);
+}
+
+namespace {
+
+int check_route(const void* x, const void* w_gate, const float* gate_bias, int T, int H, int E, int k,
+                int n_shared, int dtype, float* logits, int32_t* topk_ids, float* topk_w, void* ws,
+                size_t ws_bytes) {
   if (T < 0 || H < 1 || E < 1 || k < 1 || n_shared < 0 || k > E || !dtype_ok(dtype)) return MOE_EINVAL;
   if (E > MAX_E || k > MAX_K || k + n_shared > MAX_KK || !k_len_ok(H, dtype)) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
@@ -68,8 +93,44 @@ int moe_route(const void* x, const void* w_gate, const float* gate_bias, int T, 
   if (!aligned16(x) || !aligned16(w_gate) || !aligned4(logits) || !aligned4(topk_ids) ||
       !aligned4(topk_w) || (gate_bias && !aligned4(gate_bias)))
     return MOE_EINVAL;
-  launch_gate_gemm(dtype, x, w_gate, gate_bias, logits, T, H, E, stream);
-  launch_topk(logits, T, E, k, renorm ? 1 : 0, n_shared, topk_ids, topk_w, stream);
+  if (!ws || !aligned16(ws) || ws_bytes < route_workspace_bytes(T, H, E, dtype)) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+int moe_route(const void* x, const void* w_gate, const float* gate_bias, int T, int H, int E, int k,
+              int renorm, int n_shared, int dtype, float* logits, int32_t* topk_ids, float* topk_w,
+              void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int st = check_route(x, w_gate, gate_bias, T, H, E, k, n_shared, dtype, logits, topk_ids, topk_w,
+                             ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  launch_route(dtype, x, w_gate, gate_bias, logits, topk_ids, topk_w, T, H, E, k, renorm ? 1 : 0,
+               n_shared, ws, 0, 1, nullptr, nullptr, nullptr, nullptr, stream);
+  return launched();
+}
+
+int moe_route_permute(const void* x, const void* w_gate, const float* gate_bias, int T, int H, int E,
+                      int k, int renorm, int n_shared, int dtype, float* logits, int32_t* topk_ids,
+                      float* topk_w, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,
+                      int32_t* sorted_pair, int32_t* pair_pos, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  int st = check_route(x, w_gate, gate_bias, T, H, E, k, n_shared, dtype, logits, topk_ids, topk_w, ws,
+                       ws_bytes);
+  if (st != MOE_OK) return st;
+  if (g_begin < 0 || n_groups < 1) return MOE_EINVAL;
+  if (n_groups > MAX_GROUPS) return MOE_EUNSUPPORTED;
+  if (!counts || !offsets || !aligned4(counts) || !aligned4(offsets)) return MOE_EINVAL;
+  if (T > 0 && (!sorted_pair || !pair_pos || !aligned4(sorted_pair) || !aligned4(pair_pos)))
+    return MOE_EINVAL;
+  if (T == 0) {
+    // nothing is routed: the counts and offsets of an empty batch
+    launch_permute(topk_ids, 0, k + n_shared, g_begin, n_groups, counts, offsets, sorted_pair,
+                   pair_pos, stream);
+    return launched();
+  }
+  launch_route(dtype, x, w_gate, gate_bias, logits, topk_ids, topk_w, T, H, E, k, renorm ? 1 : 0,
+               n_shared, ws, g_begin, n_groups, counts, offsets, sorted_pair, pair_pos, stream);
   return launched();
 }
 

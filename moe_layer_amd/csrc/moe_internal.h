@@ -15,16 +15,18 @@ constexpr int MAX_E = 512;        // routed experts in the gate (8 logits per la
 constexpr int MAX_K = 32;         // routed picks per token
 constexpr int MAX_KK = 64;        // routed + shared slots per token
 constexpr int MAX_P = 64;         // peers in a repack
-constexpr int MAX_KSPLIT = 16;    // waves splitting K inside one block
 
 int device_cu_count();
 
-// gate GEMM: logits (T,E) fp32 = x (T,H) . Wg (E,H)^T + b
-void launch_gate_gemm(int dtype, const void* x, const void* wg, const float* bias, float* logits,
-                      int T, int H, int E, hipStream_t s);
-// softmax + top-k (+ renorm, + shared slots)
-void launch_topk(const float* logits, int T, int E, int k, int renorm, int n_shared,
-                 int32_t* ids, float* w, hipStream_t s);
+// gate GEMM + softmax + top-k (+ renorm, + shared slots) in one launch, and,
+// when `counts` is non-null, the stable permutation of the pairs as well.
+// ws: route_workspace_bytes() bytes whose counter head is zero on entry (and
+// is left zero).
+size_t route_workspace_bytes(int T, int H, int E, int dtype);
+void launch_route(int dtype, const void* x, const void* wg, const float* bias, float* logits,
+                  int32_t* ids, float* w, int T, int H, int E, int k, int renorm, int n_shared,
+                  void* ws, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,
+                  int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s);
 // counts, offsets, stable permutation
 void launch_permute(const int32_t* ids, int T, int kk, int g_begin, int n_groups, int32_t* counts,
                     int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s);

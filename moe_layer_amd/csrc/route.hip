@@ -1,104 +1,392 @@
-// Softmax + top-k routing (Sem-MoE notes, Key design 1: top-k of the softmax
-// of the gate logits).  One wavefront per token.
+// Routing in one launch: gate GEMM, softmax + top-k, and (optionally) the
+// stable permutation of pairs by expert (Sem-MoE notes, Key design 1: the
+// gate is top-k(softmax(W_g h + b_g)); Key design 4: the argsort of tokens by
+// expert).
 //
-// Lane l holds logits of experts l, l+64, ... (up to 8).  Each of the k rounds
-// takes every lane's best remaining (value, id) and reduces the wave with a
-// xor-butterfly under the order "larger value first, then lower expert id";
-// that order is total, so every lane ends with the same winner and equal
-// logits (including -0.0 vs +0.0) always go to the lower id.  Lane j keeps the
-// j-th pick.  Selection is on the fp32 logits, which picks the same set as
-// the softmax.  The softmax weights use the row maximum (the first pick); the
-// butterfly sums are commutative at every level, so every lane sees the same
-// bits.  Shared experts follow the routed slots as ids E, E+1, ... with
-// weight 1.
+// Phase A -- gate GEMM.  logits[t, e] = sum_h x[t, h] W_g[e, h] + b[e] is cut
+//   into units of 16 experts x 16 tokens x one K-slice; each wave computes a
+//   unit with 16x16 MFMA tiles (lane l: expert/token row l%16, bytes
+//   16*(l/16) of each 64-byte K fragment) and writes its partial tile.  K is
+//   split into KS slices (a power of two; trailing slices may be empty) so
+//   that small batches still spread the gate matrix over many CUs.  All
+//   blocks of one 16-token tile share a counter.
+// Phase B -- the block that completes a token tile's counter (the last one to
+//   arrive; integer atomics, nobody waits) sums the KS partials of each of
+//   the tile's logits in slice order, adds the bias and writes the logits
+//   (to HBM and to LDS), then runs the top-k of each token, one wave per
+//   token: lane l holds experts l, l+64, ...; each of the k rounds reduces
+//   (value, id) over the wave with a xor-butterfly under "larger value
+//   first, then lower id" -- a total order, so every lane sees the same
+//   winner and equal logits (-0.0 vs +0.0 included) go to the lower id.
+//   Selection is on the fp32 logits (the same set as on the softmax).
+//   Weights: softmax over all E routed experts at the picks, optionally
+//   renormalised over the k picks; shared experts E, E+1, ... follow with
+//   weight 1.  All butterfly sums are commutative at every level, so every
+//   lane holds the same bits.
+// Phase C -- the block that completes the last token tile (second counter)
+//   runs the stable counting sort of all T*kk pairs (sort.hpp).
+// Counters live in the caller's workspace; each finishing block resets the
+// counter it completed, so the workspace is zero again after every call.
+// Everything one block hands to another (partial tiles, logits of the
+// un-split case, top-k ids) is written and read with agent-scope relaxed
+// accesses, which stay coherent across the XCDs' L2 caches; a fence would
+// instead write back and invalidate the whole L2 of every arriving block.
 #include <math.h>
 
 #include "common.hpp"
 #include "moe_internal.h"
+#include "sort.hpp"
 
 namespace moe {
 
-constexpr int TOPK_WAVES = 4;
-constexpr int MAX_PER_LANE = MAX_E / WAVE;
+constexpr int RT_WAVES = 8;
+constexpr int RT_THREADS = RT_WAVES * WAVE;
+constexpr int RT_CHUNK = 8;                // K fragments per inner step
+constexpr int RT_MAX_KS = 16;              // K slices at most (a power of two)
+constexpr int RT_KEY_CAP = 16 * MAX_E * 2; // 16-bit sort keys that fit the logit tile's LDS
+constexpr int RT_UNROLL = 4;               // logits each thread reduces per pass of phase B
+constexpr int N_XCD = 8;
 
-__global__ __launch_bounds__(TOPK_WAVES * WAVE) void topk_kernel(const float* __restrict__ logits,
-                                                                  int T, int E, int k, int renorm,
-                                                                  int n_shared,
-                                                                  int32_t* __restrict__ ids,
-                                                                  float* __restrict__ w) {
-  const int t = blockIdx.x * TOPK_WAVES + threadIdx.x / WAVE;
-  if (t >= T) return;  // whole wave leaves together
-  const int l = lane_id();
-  const int kk = k + n_shared;
-  const float* row = logits + static_cast<size_t>(t) * E;
+struct RouteArgs {
+  const void* x;
+  const void* wg;
+  const float* bias;       // nullable
+  float* logits;           // (T, E)
+  int32_t* ids;            // (T, kk)
+  float* w;                // (T, kk)
+  float* partial;          // (KS, T, E) when KS > 1
+  int* ctr;                // n_tt + 1 counters
+  // permutation outputs (null: routing only)
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_pos;
+  int g_begin, n_groups;
+  int T, H, E, k, renorm, n_shared;
+  int kfrag_total;         // H * elem / 64
+  int kf;                  // fragments per slice
+  int n_et;                // 16-expert tiles
+  int n_tt;                // 16-token tiles
+  int bpt;                 // blocks per token tile
+};
 
-  float v[MAX_PER_LANE];
+// Top-k of one token by a group of 16 lanes (4 tokens per wave): lane r of
+// the group holds experts r, r+16, r+32, ... as 64-bit keys
+//   (order-preserving image of the fp32 logit) << 32 | (2^32 - 1 - expert)
+// so that one unsigned max picks the larger logit and, among equal logits
+// (-0.0 and +0.0 included), the lower expert id.  Each of the k rounds takes
+// the lane maxima, reduces them over the group with DPP moves (quad xor 1,
+// quad xor 2, half-row mirror, row mirror: every lane ends with the same
+// winner) and clears the winner's key.  Selection is on the fp32 logits,
+// the same set as on the softmax.
+constexpr int TK_LANES = 16;
+constexpr int TK_MAXV = MAX_E / TK_LANES;
+
+__device__ __forceinline__ uint64_t logit_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;  // -0.0 ties with +0.0
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | (0xffffffffu - static_cast<uint32_t>(e));
+}
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t u = static_cast<uint32_t>(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) {
+  return static_cast<int>(0xffffffffu - static_cast<uint32_t>(key));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
+  const uint64_t o = (static_cast<uint64_t>(dpp32<CTRL>(static_cast<uint32_t>(v >> 32))) << 32) |
+                     dpp32<CTRL>(static_cast<uint32_t>(v));
+  return o > v ? o : v;
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __uint_as_float(dpp32<CTRL>(__float_as_uint(v)));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7 - i within 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15 - i within 16
+
+__device__ __forceinline__ uint64_t group16_max(uint64_t v) {
+  v = dpp_max<DPP_XOR1>(v);
+  v = dpp_max<DPP_XOR2>(v);
+  v = dpp_max<DPP_HALF_MIRROR>(v);
+  return dpp_max<DPP_MIRROR>(v);
+}
+// Every lane of the group gets the same bits: each level adds two equal
+// partial sums in either order, and fp32 addition is commutative.
+__device__ __forceinline__ float group16_sum(float v) {
+  v = dpp_add<DPP_XOR1>(v);
+  v = dpp_add<DPP_XOR2>(v);
+  v = dpp_add<DPP_HALF_MIRROR>(v);
+  return dpp_add<DPP_MIRROR>(v);
+}
+
+// lg: the token's E logits (LDS), E <= 16 * V.  All 16 lanes of the group
+// call this.  Weights: softmax over all E routed experts at the picks,
+// optionally renormalised over the k picks; shared experts E, E+1, ...
+// follow with weight 1.
+template <int V>
+__device__ __forceinline__ void group_topk(const float* lg, int E, int k, int renorm, int n_shared,
+                                           int32_t* ids, float* w) {
+  const int r = lane_id() & (TK_LANES - 1);
+  uint64_t key[V];  // key 0 never wins: every real key is larger
 #pragma unroll
-  for (int j = 0; j < MAX_PER_LANE; ++j) {
-    const int e = l + WAVE * j;
-    v[j] = (e < E) ? row[e] : -INFINITY;
+  for (int j = 0; j < V; ++j) {
+    const int e = r + TK_LANES * j;
+    key[j] = e < E ? logit_key(lg[e], e) : 0ull;
   }
-  unsigned taken = 0;  // bit j: expert l + 64 j already picked (or absent)
-#pragma unroll
-  for (int j = 0; j < MAX_PER_LANE; ++j)
-    if (l + WAVE * j >= E) taken |= 1u << j;
-
-  float my_v = -INFINITY;
-  int my_e = -1;
+  uint64_t pick0 = 0, pick1 = 0;  // this lane's picks: rounds r and r + 16
   for (int round = 0; round < k; ++round) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < MAX_PER_LANE; ++j) {
-      const int e = l + WAVE * j;
-      if (!((taken >> j) & 1u) && (be == 0x7fffffff || v[j] > bv)) {
-        bv = v[j];
-        be = e;
-      }
-    }
+    for (int j = 0; j < V; ++j) best = key[j] > best ? key[j] : best;
+    best = group16_max(best);
 #pragma unroll
-    for (int off = WAVE / 2; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, WAVE);
-      const int oe = __shfl_xor(be, off, WAVE);
-      if (oe != 0x7fffffff && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be))) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & (WAVE - 1)) == l) taken |= 1u << (be / WAVE);
-    if (l == round) {
-      my_v = bv;
-      my_e = be;
+    for (int j = 0; j < V; ++j) key[j] = key[j] == best ? 0ull : key[j];
+    if (r == (round & (TK_LANES - 1))) {
+      if (round < TK_LANES) pick0 = best;
+      else pick1 = best;
     }
   }
-
-  const float mx = __shfl(my_v, 0, WAVE);
+  // max logit = the first pick, held by lane 0 of the group
+  const float mx = key_logit(static_cast<uint64_t>(__shfl(static_cast<long long>(pick0),
+                                                          lane_id() & ~(TK_LANES - 1), WAVE)));
   float s_all = 0.f;
 #pragma unroll
-  for (int j = 0; j < MAX_PER_LANE; ++j)
-    if (l + WAVE * j < E) s_all += expf(v[j] - mx);
-  float p = (l < k) ? expf(my_v - mx) : 0.f;
-  float s_sel = p;
-#pragma unroll
-  for (int off = WAVE / 2; off > 0; off >>= 1) {
-    s_all += __shfl_xor(s_all, off, WAVE);
-    s_sel += __shfl_xor(s_sel, off, WAVE);
+  for (int j = 0; j < V; ++j) {
+    const int e = r + TK_LANES * j;
+    if (e < E) s_all += expf(lg[e] - mx);
   }
+  const float p0 = (r < k) ? expf(key_logit(pick0) - mx) : 0.f;
+  const float p1 = (r + TK_LANES < k) ? expf(key_logit(pick1) - mx) : 0.f;
+  s_all = group16_sum(s_all);
+  const float s_sel = group16_sum(p0 + p1);
   const float denom = renorm ? s_sel : s_all;
-  if (l < k) {
-    ids[static_cast<size_t>(t) * kk + l] = my_e;
-    w[static_cast<size_t>(t) * kk + l] = p / denom;
-  } else if (l < kk) {
-    ids[static_cast<size_t>(t) * kk + l] = E + (l - k);
-    w[static_cast<size_t>(t) * kk + l] = 1.0f;
+  if (r < k) {
+    st_agent(ids + r, key_expert(pick0));
+    w[r] = p0 / denom;
+  }
+  if (r + TK_LANES < k) {
+    st_agent(ids + r + TK_LANES, key_expert(pick1));
+    w[r + TK_LANES] = p1 / denom;
+  }
+  for (int sh = r; sh < n_shared; sh += TK_LANES) {
+    st_agent(ids + k + sh, E + sh);
+    w[k + sh] = 1.0f;
   }
 }
 
-void launch_topk(const float* logits, int T, int E, int k, int renorm, int n_shared, int32_t* ids,
-                 float* w, hipStream_t s) {
-  const int grid = (T + TOPK_WAVES - 1) / TOPK_WAVES;
-  hipLaunchKernelGGL(topk_kernel, dim3(grid), dim3(TOPK_WAVES * WAVE), 0, s, logits, T, E, k,
-                     renorm, n_shared, ids, w);
+template <typename T, int KS>
+__global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
+  __shared__ int s_cnt[RT_WAVES * MAX_GROUPS];
+  __shared__ int s_off[MAX_GROUPS];
+  __shared__ float s_lg[16 * MAX_E];  // the tile's logits; later the sort's 16-bit keys
+  __shared__ int s_last;              // hand-off flag
+
+  // XCD-aware order: hardware deals blocks to the 8 XCDs round-robin, so
+  // logical block b runs on XCD b / (grid / 8) and the blocks of one token
+  // tile share an L2 (its activation rows are fetched from HBM once).
+  const int per_xcd = gridDim.x / N_XCD;
+  const int lb = (blockIdx.x % N_XCD) * per_xcd + blockIdx.x / N_XCD;
+  if (lb >= a.n_tt * a.bpt) return;  // padding to a multiple of 8 blocks
+
+  const int tid = threadIdx.x;
+  const int wv = tid / WAVE;
+  const int l = lane_id();
+  const int lrow = l & 15;
+  const int lq = l >> 4;
+  const int tt = lb / a.bpt;
+  const int unit = (lb % a.bpt) * RT_WAVES + wv;
+  const size_t row_bytes = static_cast<size_t>(a.H) * sizeof(T);
+
+  // ---------------- phase A: one 16x16 partial tile per wave
+  if (unit < a.n_et * KS) {
+    const int et = unit % a.n_et;
+    const int ks = unit / a.n_et;
+    const int f_begin = ks * a.kf;
+    const int f_end = min(a.kfrag_total, f_begin + a.kf);  // empty for trailing slices
+    float b4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      b4[r] = (KS == 1 && a.bias) ? a.bias[min(et * 16 + 4 * lq + r, a.E - 1)] : 0.f;
+    const char* wp = reinterpret_cast<const char*>(a.wg) +
+                     static_cast<size_t>(min(et * 16 + lrow, a.E - 1)) * row_bytes + lq * 16;
+    const char* xp = reinterpret_cast<const char*>(a.x) +
+                     static_cast<size_t>(min(tt * 16 + lrow, a.T - 1)) * row_bytes + lq * 16;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int f0 = f_begin; f0 < f_end; f0 += RT_CHUNK) {
+      uint4 wf[RT_CHUNK], xf[RT_CHUNK];
+#pragma unroll
+      for (int i = 0; i < RT_CHUNK; ++i) {
+        const int f = min(f0 + i, f_end - 1);
+        wf[i] = ld16(wp + f * FRAG_BYTES);
+        xf[i] = ld16(xp + f * FRAG_BYTES);
+      }
+#pragma unroll
+      for (int i = 0; i < RT_CHUNK; ++i) acc = Elem<T>::mma(wf[i], keep_or_zero(f0 + i < f_end, xf[i]), acc);
+    }
+    // acc[r] = D[4*lq + r][lrow]: expert et*16 + 4*lq + r, token tt*16 + lrow.
+    const int t = tt * 16 + lrow;
+    if (t < a.T) {
+      float* dst = (KS == 1) ? a.logits + static_cast<size_t>(t) * a.E
+                             : a.partial + (static_cast<size_t>(ks) * a.T + t) * a.E;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = et * 16 + 4 * lq + r;
+        if (e < a.E) st_agent(dst + e, acc[r] + b4[r]);
+      }
+    }
+  }
+
+  // ---------------- hand-off: the last block of this token tile continues
+  if (!last_to_arrive(a.ctr + tt, a.bpt, &s_last)) return;
+
+  // ---------------- phase B1: the tile's logits into LDS (slice sums in slice order)
+  const int t0 = tt * 16;
+  const int n_tok = min(16, a.T - t0);
+  const int n_lg = n_tok * a.E;
+  const size_t slice = static_cast<size_t>(a.T) * a.E;
+  const float* src = (KS == 1) ? a.logits : a.partial;
+  for (int i0 = tid; i0 < n_lg; i0 += RT_THREADS * RT_UNROLL) {
+    float part[RT_UNROLL][KS];  // every load is issued before the first add
+#pragma unroll
+    for (int u = 0; u < RT_UNROLL; ++u) {
+      const int i = min(i0 + u * RT_THREADS, n_lg - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) part[u][ks] = ld_agent(src + ks * slice + static_cast<size_t>(t0) * a.E + i);
+    }
+#pragma unroll
+    for (int u = 0; u < RT_UNROLL; ++u) {
+      const int i = i0 + u * RT_THREADS;
+      if (i < n_lg) {
+        float s = part[u][0];
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) s += part[u][ks];
+        if (KS > 1) {
+          s += a.bias ? a.bias[i % a.E] : 0.f;
+          a.logits[static_cast<size_t>(t0) * a.E + i] = s;
+        }
+        s_lg[i] = s;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---------------- phase B2: top-k of the tile's tokens, 16 lanes per token
+  const int kk = a.k + a.n_shared;
+  {
+    const int j = tid / TK_LANES;  // group-uniform
+    if (j < n_tok) {
+      const size_t t = static_cast<size_t>(t0 + j);
+      const float* lg = s_lg + j * a.E;
+      int32_t* ids = a.ids + t * kk;
+      float* w = a.w + t * kk;
+      if (a.E <= 4 * TK_LANES) group_topk<4>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w);
+      else if (a.E <= 8 * TK_LANES) group_topk<8>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w);
+      else if (a.E <= 16 * TK_LANES) group_topk<16>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w);
+      else group_topk<TK_MAXV>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w);
+    }
+  }
+  if (a.counts == nullptr) return;  // routing only
+
+  // ---------------- hand-off: the block finishing the last tile sorts all pairs
+  if (!last_to_arrive(a.ctr + a.n_tt, a.n_tt, &s_last)) return;
+
+  // ---------------- phase C: stable counting sort of the T*kk pairs
+  block_counting_sort<RT_WAVES, true>(a.ids, a.T * kk, a.g_begin, a.n_groups, a.counts, a.offsets,
+                                      a.sorted_pair, a.pair_pos, s_cnt, s_off,
+                                      reinterpret_cast<uint16_t*>(s_lg), RT_KEY_CAP);
+}
+
+// ---------------------------------------------------------------- host side
+
+struct RoutePlan {
+  int ks, kf, n_et, n_tt, bpt, grid;
+  size_t ctr_bytes, partial_bytes;
+};
+
+static RoutePlan plan_route(int T, int H, int E, int dtype) {
+  RoutePlan p{};
+  const int kft = H * (dtype == 1 ? 2 : 4) / FRAG_BYTES;
+  p.n_et = (E + 15) / 16;
+  p.n_tt = (T + 15) / 16;
+  // K slices (a power of two): enough wave units to spread the gate matrix
+  // and the activations over the chip (~16 waves per CU), at least 8
+  // fragments (512 bytes of each row) per slice.
+  const long long tiles = static_cast<long long>(p.n_et) * p.n_tt;
+  int ks = 1;
+  while (ks < RT_MAX_KS && tiles * ks < 4096 && kft / (2 * ks) >= 8) ks *= 2;
+  p.ks = ks;
+  p.kf = (kft + ks - 1) / ks;
+  p.bpt = (p.n_et * p.ks + RT_WAVES - 1) / RT_WAVES;
+  p.grid = (p.n_tt * p.bpt + N_XCD - 1) / N_XCD * N_XCD;
+  p.ctr_bytes = ((static_cast<size_t>(p.n_tt) + 1) * sizeof(int) + 255) & ~static_cast<size_t>(255);
+  p.partial_bytes = p.ks > 1 ? static_cast<size_t>(p.ks) * T * E * sizeof(float) : 0;
+  return p;
+}
+
+size_t route_workspace_bytes(int T, int H, int E, int dtype) {
+  if (T <= 0) return 0;
+  const RoutePlan p = plan_route(T, H, E, dtype);
+  return p.ctr_bytes + p.partial_bytes;
+}
+
+template <typename T>
+static void launch_route_t(const RoutePlan& p, const RouteArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(p.grid)), block(RT_THREADS);
+  switch (p.ks) {
+    case 1: hipLaunchKernelGGL((route_kernel<T, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((route_kernel<T, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((route_kernel<T, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((route_kernel<T, 8>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((route_kernel<T, 16>), grid, block, 0, s, a); break;
+  }
+}
+
+void launch_route(int dtype, const void* x, const void* wg, const float* bias, float* logits,
+                  int32_t* ids, float* w, int T, int H, int E, int k, int renorm, int n_shared,
+                  void* ws, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,
+                  int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s) {
+  const RoutePlan p = plan_route(T, H, E, dtype);
+  RouteArgs a{};
+  a.x = x;
+  a.wg = wg;
+  a.bias = bias;
+  a.logits = logits;
+  a.ids = ids;
+  a.w = w;
+  a.ctr = static_cast<int*>(ws);
+  a.partial = p.ks > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.ctr_bytes) : nullptr;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.sorted_pair = sorted_pair;
+  a.pair_pos = pair_pos;
+  a.g_begin = g_begin;
+  a.n_groups = n_groups;
+  a.T = T;
+  a.H = H;
+  a.E = E;
+  a.k = k;
+  a.renorm = renorm;
+  a.n_shared = n_shared;
+  a.kfrag_total = H * (dtype == 1 ? 2 : 4) / FRAG_BYTES;
+  a.kf = p.kf;
+  a.n_et = p.n_et;
+  a.n_tt = p.n_tt;
+  a.bpt = p.bpt;
+  if (dtype == 1)
+    launch_route_t<uint16_t>(p, a, s);
+  else
+    launch_route_t<float>(p, a, s);
 }
 
 }  // namespace moe

@@ -4,9 +4,10 @@
 calls need for a given shape, once, so repeated passes allocate nothing and
 can be captured in a HIP graph.  ``moe_layer_forward`` enqueues
 
-    moe_route -> moe_permute -> moe_expert_up -> moe_expert_down -> moe_combine
+    moe_route_permute -> moe_expert_up -> moe_expert_down -> moe_combine
 
-on the current stream.  All arithmetic happens in the HIP library.
+(four launches) on the current stream; ``fused=False`` runs moe_route and
+moe_permute as two calls instead.  All arithmetic happens in the HIP library.
 """
 from dataclasses import dataclass
 
@@ -27,6 +28,7 @@ class MoeLayerBuffers:
     a: torch.Tensor
     y_pair: torch.Tensor
     y: torch.Tensor
+    route_ws: torch.Tensor
 
     @classmethod
     def allocate(cls, T, H, E, kk, n_groups, I, dtype, device="cuda"):
@@ -45,11 +47,12 @@ class MoeLayerBuffers:
             a=torch.empty((T * kk, I), **act),
             y_pair=torch.empty((T * kk, H), **act),
             y=torch.empty((T, H), **act),
+            route_ws=_lib.route_workspace(T, H, E, dtype, dev),
         )
 
 
 def moe_layer_forward(x, w_gate, gate_bias, w13, w2, k, renorm, n_shared=0, g_begin=0,
-                      bufs=None, stream=None):
+                      bufs=None, stream=None, fused=True):
     """Run the layer; returns the buffers (``bufs.y`` is the output).
 
     x (T, H); w_gate (E, H); gate_bias (E,) fp32 or None; w13 (G, 2I, H);
@@ -63,10 +66,15 @@ def moe_layer_forward(x, w_gate, gate_bias, w13, w2, k, renorm, n_shared=0, g_be
     kk = k + n_shared
     if bufs is None:
         bufs = MoeLayerBuffers.allocate(T, H, E, kk, G, I, x.dtype, x.device)
-    _lib.moe_route(x, w_gate, gate_bias, k, renorm, n_shared, bufs.logits, bufs.topk_ids,
-                   bufs.topk_w, stream)
-    _lib.moe_permute(bufs.topk_ids, g_begin, G, bufs.counts, bufs.offsets, bufs.sorted_pair,
-                     bufs.pair_pos, stream)
+    if fused:
+        _lib.moe_route_permute(x, w_gate, gate_bias, k, renorm, n_shared, bufs.logits,
+                               bufs.topk_ids, bufs.topk_w, g_begin, G, bufs.counts, bufs.offsets,
+                               bufs.sorted_pair, bufs.pair_pos, bufs.route_ws, stream)
+    else:
+        _lib.moe_route(x, w_gate, gate_bias, k, renorm, n_shared, bufs.logits, bufs.topk_ids,
+                       bufs.topk_w, bufs.route_ws, stream)
+        _lib.moe_permute(bufs.topk_ids, g_begin, G, bufs.counts, bufs.offsets, bufs.sorted_pair,
+                         bufs.pair_pos, stream)
     _lib.moe_expert_up(x, bufs.sorted_pair, bufs.offsets, kk, w13, bufs.a, stream)
     _lib.moe_expert_down(bufs.a, bufs.offsets, T, kk, w2, bufs.y_pair, stream)
     _lib.moe_combine(bufs.y_pair, bufs.pair_pos, bufs.topk_w, bufs.y, stream)

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     for s in range(5):
         assert L.moe_status_str(s).decode().startswith(
             ["MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP"][s])
@@ -58,8 +58,14 @@ def test_workspace_size(L):
 
 
 def route(L, x=FAKE, wg=FAKE, b=None, T=4, H=256, E=8, k=2, renorm=1, ns=0, dt=BF16,
-          lo=FAKE, ids=FAKE, w=FAKE):
-    return L.moe_route(x, wg, b, T, H, E, k, renorm, ns, dt, lo, ids, w, None)
+          lo=FAKE, ids=FAKE, w=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return L.moe_route(x, wg, b, T, H, E, k, renorm, ns, dt, lo, ids, w, ws, ws_bytes, None)
+
+
+def route_permute(L, T=4, H=256, E=8, k=2, g_begin=0, n_groups=8, counts=FAKE, ws=FAKE, ws_bytes=1 << 30,
+                  x=FAKE):
+    return L.moe_route_permute(x, FAKE, None, T, H, E, k, 1, 0, BF16, FAKE, FAKE, FAKE, g_begin, n_groups,
+                               counts, FAKE, FAKE, FAKE, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -74,14 +80,37 @@ def route(L, x=FAKE, wg=FAKE, b=None, T=4, H=256, E=8, k=2, renorm=1, ns=0, dt=B
     (dict(E=64, k=33), MOE_EUNSUPPORTED),
     (dict(k=2, ns=63), MOE_EUNSUPPORTED),    # k + n_shared > 64
     (dict(H=100), MOE_EUNSUPPORTED),         # not whole 64-byte K chunks
-    (dict(H=16384), MOE_EUNSUPPORTED),       # more than 16 waves of K
+    (dict(H=1 << 20), MOE_EUNSUPPORTED),     # rows over 1 MiB
+    (dict(ws=None), MOE_EWORKSPACE),
+    (dict(ws=MISALIGNED), MOE_EWORKSPACE),
+    (dict(ws_bytes=0), MOE_EWORKSPACE),
 ])
 def test_route_rejects(L, kw, status):
     assert route(L, **kw) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(g_begin=-1), MOE_EINVAL),
+    (dict(n_groups=0), MOE_EINVAL),
+    (dict(n_groups=513), MOE_EUNSUPPORTED),
+    (dict(counts=None), MOE_EINVAL),
+    (dict(ws_bytes=16), MOE_EWORKSPACE),
+    (dict(x=None), MOE_EINVAL),
+])
+def test_route_permute_rejects(L, kw, status):
+    assert route_permute(L, **kw) == status
+
+
+def test_route_workspace_size(L):
+    small = L.moe_route_workspace_bytes(8, 4096, 128, BF16)
+    big = L.moe_route_workspace_bytes(2048, 4096, 128, BF16)
+    assert small >= 256 and small % 256 == 0
+    assert big >= (2048 // 16 + 1) * 4
+    assert L.moe_route_workspace_bytes(0, 4096, 128, BF16) == 0
+
+
 def test_empty_batch_is_a_no_op(L):
-    assert route(L, T=0, x=None, lo=None, ids=None, w=None) == MOE_OK
+    assert route(L, T=0, x=None, lo=None, ids=None, w=None, ws=None, ws_bytes=0) == MOE_OK
     assert L.moe_combine(None, None, None, 0, 8, 256, BF16, None, None) == MOE_OK
     assert L.moe_grouped_gemm(None, None, None, 0, 8, 16, None, None, 256, 128, BF16, None, None, 0,
                               None) == MOE_OK

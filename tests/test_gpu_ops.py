@@ -232,3 +232,71 @@ def test_graph_replay_matches_eager():
         assert np.array_equal(gh.from_dev(bufs.y), want)
         eager = moe_layer_amd.moe_layer_forward(x, wg, b, w13, w2, cfg.k, cfg.renorm)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,E,k,n_shared,H", [(3000, 64, 8, 0, 256), (8, 128, 8, 0, 4096),
+                                               (40, 64, 6, 2, 2048)])
+def test_fused_route_matches_two_calls_and_leaves_workspace_zero(T, E, k, n_shared, H):
+    """One launch (routing + sort) against moe_route then moe_permute; the
+    3000-token case has more pairs than the sort stages in LDS."""
+    import torch
+
+    import gpu_helpers as gh
+    import moe_layer_amd
+    cfg = small(H=H, E=E, k=k, n_shared=n_shared, renorm=False, T=T)
+    d = make_layer_inputs(cfg, T, routing="zipf", seed=12)
+    x, wg, b = gh.to_dev(d["x"]), gh.to_dev(d["w_gate"]), gh.to_dev(d["gate_bias"])
+    kk, G = k + n_shared, E + n_shared
+    print(f"[case] fused route T={T} E={E}", flush=True)
+    outs = []
+    for fused in (True, False, True):
+        bufs = moe_layer_amd.MoeLayerBuffers.allocate(T, H, E, kk, G, cfg.I, torch.bfloat16)
+        if fused:
+            moe_layer_amd.moe_route_permute(x, wg, b, k, False, n_shared, bufs.logits, bufs.topk_ids,
+                                            bufs.topk_w, 0, G, bufs.counts, bufs.offsets,
+                                            bufs.sorted_pair, bufs.pair_pos, bufs.route_ws)
+        else:
+            moe_layer_amd.moe_route(x, wg, b, k, False, n_shared, bufs.logits, bufs.topk_ids,
+                                    bufs.topk_w, bufs.route_ws)
+            moe_layer_amd.moe_permute(bufs.topk_ids, 0, G, bufs.counts, bufs.offsets,
+                                      bufs.sorted_pair, bufs.pair_pos)
+        torch.cuda.synchronize()
+        n = moe_layer_amd.moe_route_workspace_bytes(T, H, E, 1)
+        head = (T + 15) // 16 + 1
+        assert int(bufs.route_ws[: 4 * head].count_nonzero()) == 0, "counters not reset"
+        assert n >= 4 * head
+        outs.append({k_: gh.from_dev(getattr(bufs, k_)) for k_ in
+                     ("logits", "topk_ids", "topk_w", "counts", "offsets", "pair_pos")})
+    for key in outs[0]:
+        assert np.array_equal(outs[0][key], outs[1][key]), key
+        assert np.array_equal(outs[0][key], outs[2][key]), key
+    ids_ref, w_ref = oracle.route(outs[0]["logits"].astype(np.float64), k, False, n_shared)
+    assert np.array_equal(outs[0]["topk_ids"], ids_ref)
+    assert np.abs(outs[0]["topk_w"] - w_ref).max() <= 1e-5
+    c, o, _, pos = oracle.permute(outs[0]["topk_ids"], 0, G)
+    assert np.array_equal(outs[0]["counts"], c) and np.array_equal(outs[0]["pair_pos"], pos)
+
+
+def test_route_workspace_reused_across_shapes():
+    """One zeroed workspace serves calls of different batch sizes in turn."""
+    import torch
+
+    import gpu_helpers as gh
+    import moe_layer_amd
+    cfg = small(E=32, k=4, T=300)
+    d = make_layer_inputs(cfg, 300, seed=13)
+    wg, b = gh.to_dev(d["w_gate"]), gh.to_dev(d["gate_bias"])
+    ws = moe_layer_amd.route_workspace(300, cfg.H, cfg.E, torch.bfloat16)
+    print("[case] workspace reuse", flush=True)
+    for T in (300, 5, 77, 300):
+        x = gh.to_dev(d["x"][:T])
+        bufs = moe_layer_amd.MoeLayerBuffers.allocate(T, cfg.H, cfg.E, cfg.k, cfg.E, cfg.I, torch.bfloat16)
+        moe_layer_amd.moe_route_permute(x, wg, b, cfg.k, True, 0, bufs.logits, bufs.topk_ids, bufs.topk_w,
+                                        0, cfg.E, bufs.counts, bufs.offsets, bufs.sorted_pair,
+                                        bufs.pair_pos, ws)
+        torch.cuda.synchronize()
+        ids_ref, _ = oracle.route(gh.from_dev(bufs.logits).astype(np.float64), cfg.k, True)
+        assert np.array_equal(gh.from_dev(bufs.topk_ids), ids_ref)
+        c, o, sp, pos = oracle.permute(ids_ref, 0, cfg.E)
+        assert np.array_equal(gh.from_dev(bufs.offsets), o)
+        assert np.array_equal(gh.from_dev(bufs.sorted_pair)[: o[-1]], sp)
