@@ -51,7 +51,7 @@ enum moe_status {
 enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
 
 enum moe_op { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_GROUPED_GEMM = 2, MOE_OP_COMBINE = 3,
-              MOE_OP_REPACK = 4 };
+              MOE_OP_REPACK = 4, MOE_OP_EXPERT_UP = 5, MOE_OP_EXPERT_DOWN = 6 };
 
 /* Version of this ABI (incremented on any signature change). */
 int moe_abi_version(void);
@@ -59,9 +59,18 @@ int moe_abi_version(void);
 /* Human-readable text for a status code (static storage). */
 const char* moe_status_str(int status);
 
-/* Workspace bytes `op` needs for these sizes (0 if none).  For
- * MOE_OP_GROUPED_GEMM: the (T*kk, I) intermediate activations
- * silu(W1 x) * W3 x in the storage dtype.  (Routing: moe_route_workspace_bytes.) */
+/* Workspace bytes `op` needs for these sizes (0 if none).  The sizes depend
+ * only on the arguments, not on the device.
+ *   MOE_OP_EXPERT_UP / MOE_OP_EXPERT_DOWN: the expert GEMMs' split-item
+ *     counters and per-wave fp32 partial tiles; both ops have the same size
+ *     and layout, so one buffer serves the up and the down call in turn.
+ *     Zero-fill the buffer before its first use; every completed call leaves
+ *     the counters zero again, so the buffer serves any later call with
+ *     sizes it was allocated for.
+ *   MOE_OP_GROUPED_GEMM: the (T*kk, I) intermediate activations
+ *     silu(W1 x) * W3 x in the storage dtype (256-byte aligned), followed by
+ *     the region above (same zero-fill rule).
+ * (Routing: moe_route_workspace_bytes.) */
 size_t moe_workspace_bytes(int op, int T, int kk, int n_groups, int H, int I, int dtype);
 
 /* Workspace bytes moe_route and moe_route_permute need for T tokens, hidden
@@ -134,6 +143,7 @@ int moe_permute(const int32_t* topk_ids, int T, int kk, int g_begin, int n_group
  *   w2          (n_groups, H, I) dtype
  *   y_pair      (T*kk, H) dtype [out]     first n_kept rows written
  *   ws          >= moe_workspace_bytes(MOE_OP_GROUPED_GEMM, ...) bytes, holds a
+ *               and the split-item state; zero-filled before its first use
  * Limits: H * sizeof(dtype) and I * sizeof(dtype) multiples of 64; H % 16 == 0;
  * I % 8 == 0; n_groups <= 512.
  * a is rounded to dtype before the W2 product.
@@ -144,12 +154,17 @@ int moe_grouped_gemm(const void* x, const int32_t* sorted_pair, const int32_t* o
 
 /* The two halves of moe_grouped_gemm, for callers that keep `a` themselves.
  * moe_expert_up writes a (T*kk, I) dtype; moe_expert_down reads it.  Same
- * limits as moe_grouped_gemm. */
+ * limits as moe_grouped_gemm.  ws: >= moe_workspace_bytes(MOE_OP_EXPERT_UP or
+ * MOE_OP_EXPERT_DOWN, ...) bytes, 16-byte aligned, zero-filled before its
+ * first use (each call leaves it reusable); calls sharing one ws must not
+ * overlap in time.  Results are deterministic for given sizes on a given
+ * device (the work split follows the number of compute units). */
 int moe_expert_up(const void* x, const int32_t* sorted_pair, const int32_t* offsets, int T, int kk,
-                  int n_groups, const void* w13, int H, int I, int dtype, void* a,
-                  hipStream_t stream);
+                  int n_groups, const void* w13, int H, int I, int dtype, void* a, void* ws,
+                  size_t ws_bytes, hipStream_t stream);
 int moe_expert_down(const void* a, const int32_t* offsets, int T, int kk, int n_groups,
-                    const void* w2, int H, int I, int dtype, void* y_pair, hipStream_t stream);
+                    const void* w2, int H, int I, int dtype, void* y_pair, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
 
 /*
  * moe_combine -- y[t] = sum_{j=0..kk-1, in order, pair_pos[t*kk+j] >= 0}

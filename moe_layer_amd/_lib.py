@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_layer_amd.so")
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_GEMM, MOE_OP_COMBINE, MOE_OP_REPACK = range(5)
+MOE_OP_EXPERT_UP, MOE_OP_EXPERT_DOWN = 5, 6
 
 EXPORTED = (
     "moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes",
@@ -65,9 +66,9 @@ def lib():
     L.moe_grouped_gemm.restype = _i
     L.moe_grouped_gemm.argtypes = [_p, _p, _p, _i, _i, _i, _p, _p, _i, _i, _i, _p, _p, _sz, _p]
     L.moe_expert_up.restype = _i
-    L.moe_expert_up.argtypes = [_p, _p, _p, _i, _i, _i, _p, _i, _i, _i, _p, _p]
+    L.moe_expert_up.argtypes = [_p, _p, _p, _i, _i, _i, _p, _i, _i, _i, _p, _p, _sz, _p]
     L.moe_expert_down.restype = _i
-    L.moe_expert_down.argtypes = [_p, _p, _i, _i, _i, _p, _i, _i, _i, _p, _p]
+    L.moe_expert_down.argtypes = [_p, _p, _i, _i, _i, _p, _i, _i, _i, _p, _p, _sz, _p]
     L.moe_combine.restype = _i
     L.moe_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p]
     L.moe_repack_ep_to_tp.restype = _i
@@ -189,7 +190,15 @@ def moe_grouped_gemm(x, sorted_pair, offsets, kk, w13, w2, y_pair, ws, stream=No
     _check("moe_grouped_gemm", st)
 
 
-def moe_expert_up(x, sorted_pair, offsets, kk, w13, a, stream=None):
+def expert_workspace(T, kk, n_groups, H, I, dtype, device="cuda"):
+    """A zero-filled workspace that serves both moe_expert_up and
+    moe_expert_down for these sizes (each call leaves it zeroed again)."""
+    code = MOE_DTYPE_BF16 if dtype == torch.bfloat16 else MOE_DTYPE_F32
+    n = max(moe_workspace_bytes(MOE_OP_EXPERT_UP, T, kk, n_groups, H, I, code), 256)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_expert_up(x, sorted_pair, offsets, kk, w13, a, ws, stream=None):
     T, H = x.shape
     G, two_i, _ = w13.shape
     I = two_i // 2
@@ -197,16 +206,17 @@ def moe_expert_up(x, sorted_pair, offsets, kk, w13, a, stream=None):
         _ptr(x, "x"), _ptr(sorted_pair, "sorted_pair", torch.int32, (T * kk,)),
         _ptr(offsets, "offsets", torch.int32, (G + 1,)), T, kk, G,
         _ptr(w13, "w13", x.dtype, (G, 2 * I, H)), H, I, _dtype_code(x),
-        _ptr(a, "a", x.dtype, (T * kk, I)), _stream(stream))
+        _ptr(a, "a", x.dtype, (T * kk, I)), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(stream))
     _check("moe_expert_up", st)
 
 
-def moe_expert_down(a, offsets, T, kk, w2, y_pair, stream=None):
+def moe_expert_down(a, offsets, T, kk, w2, y_pair, ws, stream=None):
     G, H, I = w2.shape
     st = lib().moe_expert_down(
         _ptr(a, "a", w2.dtype, (T * kk, I)), _ptr(offsets, "offsets", torch.int32, (G + 1,)), T, kk, G,
         _ptr(w2, "w2"), H, I, _dtype_code(w2), _ptr(y_pair, "y_pair", w2.dtype, (T * kk, H)),
-        _stream(stream))
+        _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check("moe_expert_down", st)
 
 

@@ -7,27 +7,40 @@
 //
 // Decode-shaped problems are HBM-bound: every weight byte must stream from
 // HBM exactly once while the token side (a few to a few dozen rows per
-// expert) is small and stays in L2.  The kernel is a set of independent
-// wavefronts; nothing synchronises them after start-up, so a slow load only
-// ever stalls its own wave.  Wave work item = (group g, tile of 16 weight
+// expert) is small and stays in L2.  Work item = (group g, tile of 16 weight
 // rows, pass of up to 16*NT token rows), over the full K:
 //   up   : the 16 rows are 8 gate rows and the matching 8 up rows, so
 //          SiLU(gate)*up is formed in registers;
 //   down : 16 rows of W2 = 16 output features.
-// K is walked in 512-byte chunks.  Weights are read DRAM-friendly: each load
-// instruction takes 256 contiguous bytes from each of 4 rows (non-temporal,
-// streamed once), double-buffered in registers so chunk c+1 is in flight while
-// chunk c is multiplied.  The wave then passes its 16 rows x 512 B through a
-// private LDS tile (rows padded by 16 B) to read them back in the 16x16 MFMA
-// operand layout (lane l: row l%16, bytes 16*(l/16) of each 64-byte
-// fragment); only the wave itself touches that tile, so no barrier is needed.  Token fragments of chunk c come from
-// L2 just before use and are issued ahead of the next weight chunk, so waiting
-// for them (loads retire in order) never waits for the weights in flight.
-// The stream runs across item boundaries, and the next item's token-row
-// indices are fetched one item ahead.  Token rows past the group's count
-// repeat a real row and are never stored; fragments past the end of K are
-// zero on both sides.  No atomics: every output element is written by exactly
-// one lane, so results are bit-reproducible.
+// K is walked in 512-byte chunks.
+//
+// Balance.  With every CU streaming, one CU moves only ~1/256 of the chip's
+// HBM bandwidth, so the launch lasts as long as its most loaded CU.  The
+// grid is therefore exactly the waves that fit on the chip at once, and the
+// flattened sequence of (item, chunk) is cut into equal contiguous ranges,
+// one per wave (wave w = wv * grid + block, so a partly used grid still
+// covers every CU).  An item whose chunks fall into several waves' ranges is
+// split along K: each of those waves stores its fp32 partial tile, and the
+// last of them to arrive (an integer counter per item; nobody waits) adds the
+// partials in K order and runs the epilogue.  The sum order depends only on
+// the shapes and the grid, so results are reproducible.  Waves are otherwise
+// independent: nothing synchronises them after start-up, so a slow load only
+// ever stalls its own wave.
+//
+// Weights are read DRAM-friendly: each load instruction takes 256 contiguous
+// bytes from each of 4 rows (non-temporal, streamed once), double-buffered in
+// registers so chunk c+1 is in flight while chunk c is multiplied.  The wave
+// then passes its 16 rows x 512 B through a private LDS tile (rows padded by
+// 16 B) to read them back in the 16x16 MFMA operand layout (lane l: row
+// l%16, bytes 16*(l/16) of each 64-byte fragment); only the wave itself
+// touches that tile, so no barrier is needed.  Token fragments of chunk c
+// come from L2 just before use and are issued ahead of the next weight chunk,
+// so waiting for them (loads retire in order) never waits for the weights in
+// flight.  The stream runs across item boundaries, and the next item's
+// token-row indices are fetched one item ahead.  Token rows past the group's
+// count repeat a real row and are never stored; fragments past the end of K
+// are zero on both sides.  Every output element is written by exactly one
+// lane.
 #include "common.hpp"
 #include "moe_internal.h"
 
@@ -36,6 +49,9 @@ namespace moe {
 constexpr int XW_WAVES = 4;                             // waves per block (independent)
 constexpr int CHUNK_FRAGS = 8;                          // 64-byte fragments per chunk
 constexpr int CHUNK_BYTES = CHUNK_FRAGS * FRAG_BYTES;   // 512
+constexpr int MIN_CPW = 4;                              // chunks per wave at least (bounds split items)
+constexpr int MAX_WAVES = 4096;                         // waves of one launch at most
+constexpr int NT_MAX = 2;
 
 enum XMode { XMODE_UP = 0, XMODE_DOWN = 1 };
 
@@ -52,6 +68,10 @@ struct XArgs {
   int H;
   int kfrag_total;         // K * elem / 64
   int n_tiles;             // 16-row weight tiles per group
+  int nck;                 // 512-byte chunks per item
+  int waves;               // waves launched
+  int* ctr;                // per-item arrival counters (zero between calls)
+  float* part;             // per-wave partial tiles: [wave][2][NT][64 lanes][4]
 };
 
 // Wave 0: s_off[g] = offsets[g]; s_pstart[g] = number of mp-row passes of the
@@ -84,10 +104,13 @@ struct WItem {
   int tok[NT];             // activation row of this lane's token in each 16-row tile
 };
 
+// Weight side of an item: group, row window and the lane's 4 row pointers
+// (needs only the pass table, so the first weight loads can be issued before
+// any token index is known).
 template <typename T, int MODE, int NT>
-__device__ __forceinline__ void witem_setup(const XArgs& a, const int* s_pstart, const int* s_off,
-                                            int item, int lrow, int lq, size_t row_bytes,
-                                            WItem<NT>& it) {
+__device__ __forceinline__ void witem_weights(const XArgs& a, const int* s_pstart, const int* s_off,
+                                              int item, int lrow, int lq, size_t row_bytes,
+                                              WItem<NT>& it) {
   const int pi = item / a.n_tiles;
   const int nt = item % a.n_tiles;
   int lo = 0, hi = a.n_groups;  // s_pstart[lo] <= pi < s_pstart[hi]
@@ -116,11 +139,24 @@ __device__ __forceinline__ void witem_setup(const XArgs& a, const int* s_pstart,
     }
     it.wp[j] = reinterpret_cast<const char*>(a.w) + wrow * row_bytes + lrow * 16;
   }
+}
+
+// Token side: the activation row of this lane's token in each 16-row tile.
+template <typename T, int MODE, int NT>
+__device__ __forceinline__ void witem_tokens(const XArgs& a, int lrow, WItem<NT>& it) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     const int r = it.row0 + min(it.t0 + tt * 16 + lrow, it.m - 1);
     it.tok[tt] = (MODE == XMODE_UP) ? a.sorted_pair[r] / a.kk : r;
   }
+}
+
+template <typename T, int MODE, int NT>
+__device__ __forceinline__ void witem_setup(const XArgs& a, const int* s_pstart, const int* s_off,
+                                            int item, int lrow, int lq, size_t row_bytes,
+                                            WItem<NT>& it) {
+  witem_weights<T, MODE, NT>(a, s_pstart, s_off, item, lrow, lq, row_bytes, it);
+  witem_tokens<T, MODE, NT>(a, lrow, it);
 }
 
 // Weight bytes of chunk c in the load layout: register i holds row
@@ -216,6 +252,68 @@ __device__ __forceinline__ void wstore(const XArgs& a, const WItem<NT>& it, f32x
   }
 }
 
+// Wave that owns chunk q when Q chunks are cut into W ranges [Q*w/W, Q*(w+1)/W).
+__device__ __forceinline__ int chunk_owner(long long q, long long Q, int W) {
+  return static_cast<int>(((q + 1) * W - 1) / Q);
+}
+
+// A wave's partial of an item goes to slot 0 if the item is the first one its
+// range touches, else to slot 1 (a range has at most two split items).
+__device__ __forceinline__ float* part_slot(const XArgs& a, int NT, int w, int item, long long Q, int W) {
+  const long long q0 = Q * w / W;
+  const int which = (q0 / a.nck == item) ? 0 : 1;
+  return a.part + (static_cast<size_t>(w) * 2 + which) * NT * WAVE * 4;
+}
+
+// The item's chunks were split over waves wa..wb (K order).  Store this
+// wave's partial; the last wave to arrive sums all of them in K order and
+// runs the epilogue.
+template <typename T, int MODE, int NT>
+__device__ __forceinline__ void finish_split(const XArgs& a, const WItem<NT>& it, f32x4_t (&acc)[NT],
+                                             int item, int w, int W, long long Q, int lrow, int lq) {
+  const int l = lane_id();
+  const long long qa = static_cast<long long>(item) * a.nck;
+  const int wa = chunk_owner(qa, Q, W);
+  const int wb = chunk_owner(qa + a.nck - 1, Q, W);
+  uint64_t* mine = reinterpret_cast<uint64_t*>(part_slot(a, NT, w, item, Q, W));
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    st_agent(mine + (tt * WAVE + l) * 2, (static_cast<uint64_t>(__float_as_uint(acc[tt][1])) << 32) |
+                                             __float_as_uint(acc[tt][0]));
+    st_agent(mine + (tt * WAVE + l) * 2 + 1, (static_cast<uint64_t>(__float_as_uint(acc[tt][3])) << 32) |
+                                                 __float_as_uint(acc[tt][2]));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the partial is performed (agent scope) before the count
+  int old = 0;
+  if (l == 0) old = atomicAdd(a.ctr + item, 1);
+  old = __shfl(old, 0, WAVE);
+  if (old == wb - wa) {  // last to arrive (wave-uniform)
+    if (l == 0) st_agent(a.ctr + item, 0);
+    f32x4_t sum[NT];
+    for (int v = wa; v <= wb; ++v) {
+      f32x4_t pv[NT];
+      if (v == w) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) pv[tt] = acc[tt];
+      } else {
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(part_slot(a, NT, v, item, Q, W));
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          const uint64_t lo = ld_agent(src + (tt * WAVE + l) * 2);
+          const uint64_t hi = ld_agent(src + (tt * WAVE + l) * 2 + 1);
+          pv[tt] = f32x4_t{__uint_as_float(static_cast<uint32_t>(lo)), __uint_as_float(static_cast<uint32_t>(lo >> 32)),
+                           __uint_as_float(static_cast<uint32_t>(hi)), __uint_as_float(static_cast<uint32_t>(hi >> 32))};
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) sum[tt] = (v == wa) ? pv[tt] : sum[tt] + pv[tt];
+    }
+    wstore<T, MODE, NT>(a, it, sum, lrow, lq);
+  }
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
 template <typename T, int MODE, int NT>
 __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   __shared__ int s_pstart[MAX_GROUPS + 1];
@@ -229,36 +327,43 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
 
   pass_prefix(a.offsets, a.n_groups, 16 * NT, s_pstart, s_off);
   __syncthreads();  // the only barrier; waves are independent from here on
-  const int total = s_pstart[a.n_groups] * a.n_tiles;
-  const int stride = gridDim.x * XW_WAVES;
-  int item = blockIdx.x * XW_WAVES + wv;
-  if (item >= total) return;  // wave-uniform
+  const long long Q = static_cast<long long>(s_pstart[a.n_groups]) * a.n_tiles * a.nck;
+  const int W = static_cast<int>(min(static_cast<long long>(a.waves), (Q + MIN_CPW - 1) / MIN_CPW));
+  const int w = wv * gridDim.x + blockIdx.x;
+  if (w >= W) return;  // wave-uniform
+  const long long q0 = Q * w / W;
+  const long long q1 = Q * (w + 1) / W;
+  if (q0 >= q1) return;
 
   const size_t row_bytes = static_cast<size_t>(a.K) * sizeof(T);
-  const int nck = (a.kfrag_total + CHUNK_FRAGS - 1) / CHUNK_FRAGS;
   const char* act = reinterpret_cast<const char*>(a.act);
 
+  int item = static_cast<int>(q0 / a.nck);
+  int cb = static_cast<int>(q0 - static_cast<long long>(item) * a.nck);   // first chunk of the item here
+  int ce = static_cast<int>(min(static_cast<long long>(a.nck), q1 - static_cast<long long>(item) * a.nck));
+  // The first weight chunk goes out before the token indices are fetched.
   WItem<NT> cur, nxt;
-  witem_setup<T, MODE, NT>(a, s_pstart, s_off, item, lrow, lq, row_bytes, cur);
-  bool have_nxt = item + stride < total;
-  if (have_nxt) witem_setup<T, MODE, NT>(a, s_pstart, s_off, item + stride, lrow, lq, row_bytes, nxt);
+  witem_weights<T, MODE, NT>(a, s_pstart, s_off, item, lrow, lq, row_bytes, cur);
+  uint4 w0[CHUNK_FRAGS], w1[CHUNK_FRAGS], x[NT][CHUNK_FRAGS];
+  int c = cb;
+  wload(cur.wp, c, a.kfrag_total, lrow, w0);
+  witem_tokens<T, MODE, NT>(a, lrow, cur);
+  bool have_nxt = static_cast<long long>(item + 1) * a.nck < q1;
+  if (have_nxt) witem_setup<T, MODE, NT>(a, s_pstart, s_off, item + 1, lrow, lq, row_bytes, nxt);
 
   f32x4_t acc[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint4 w0[CHUNK_FRAGS], w1[CHUNK_FRAGS], x[NT][CHUNK_FRAGS];
   char* tile = s_wt[wv];
-  wload(cur.wp, 0, a.kfrag_total, lrow, w0);
-  int c = 0;
 
   // One step: token fragments of (cur, c); weights of the next chunk into WN;
-  // multiply WC; at the end of an item store it and move on (break when the
-  // wave has no more work).
+  // multiply WC; at the end of the item's chunks in this range, finish it and
+  // move on (break when the range is done).
 #define XSTEP(WC, WN)                                                                     \
   {                                                                                       \
     xload<NT>(act, cur.tok, row_bytes, lq, c, a.kfrag_total, x);                          \
     __builtin_amdgcn_sched_barrier(0); /* token loads stay ahead of the weight loads */   \
-    const bool last = c + 1 >= nck;                                                       \
+    const bool last = c + 1 >= ce;                                                        \
     /* One weight load on every path (next chunk, next item's first chunk, or with no  */ \
     /* work left a harmless re-read of this chunk), so the same number of loads is     */ \
     /* outstanding whichever way the step went and no wait drains the prefetch.        */ \
@@ -277,14 +382,19 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
     if (!last) {                                                                          \
       ++c;                                                                                \
     } else {                                                                              \
-      wstore<T, MODE, NT>(a, cur, acc, lrow, lq);                                         \
+      if (cb == 0 && ce == a.nck)                                                         \
+        wstore<T, MODE, NT>(a, cur, acc, lrow, lq);                                       \
+      else                                                                                \
+        finish_split<T, MODE, NT>(a, cur, acc, item, w, W, Q, lrow, lq);                  \
       if (!have_nxt) break;                                                               \
-      item += stride;                                                                     \
+      ++item;                                                                             \
       cur = nxt;                                                                          \
+      cb = 0;                                                                             \
       c = 0;                                                                              \
-      have_nxt = item + stride < total;                                                   \
+      ce = static_cast<int>(min(static_cast<long long>(a.nck), q1 - static_cast<long long>(item) * a.nck)); \
+      have_nxt = static_cast<long long>(item + 1) * a.nck < q1;                           \
       if (have_nxt)                                                                       \
-        witem_setup<T, MODE, NT>(a, s_pstart, s_off, item + stride, lrow, lq, row_bytes, nxt); \
+        witem_setup<T, MODE, NT>(a, s_pstart, s_off, item + 1, lrow, lq, row_bytes, nxt);  \
     }                                                                                     \
   }
 
@@ -306,29 +416,102 @@ static int pick_nt(int T, int kk, int n_groups) {
   return (mean > 12.0 && T > 16) ? 2 : 1;
 }
 
-template <int MODE, int NT>
-static void launch_x(int dtype, const XArgs& a, int T, int kk, hipStream_t s) {
+struct XShape {
+  int n_tiles, kfrag_total, nck;
+};
+
+static XShape x_shape(int mode, int H, int I, int dtype) {
+  XShape s{};
+  const int K = mode == XMODE_UP ? H : I;
+  s.n_tiles = mode == XMODE_UP ? (I + 7) / 8 : (H + 15) / 16;
+  s.kfrag_total = K * elem_bytes_x(dtype) / FRAG_BYTES;
+  s.nck = (s.kfrag_total + CHUNK_FRAGS - 1) / CHUNK_FRAGS;
+  return s;
+}
+
+// Items of one launch at most: sum over groups of ceil(m_g / 16) passes
+// <= pairs / 16 + touched groups (NT = 1 is the largest count).
+static long long max_items(const XShape& s, int T, int kk, int n_groups) {
   const long long pairs = static_cast<long long>(T) * kk;
-  const long long touched = a.n_groups < pairs ? a.n_groups : pairs;
-  const long long max_items = (pairs / (16 * NT) + touched) * a.n_tiles;
-  long long grid = (max_items + XW_WAVES - 1) / XW_WAVES;
-  const long long cap = static_cast<long long>(device_cu_count()) * 8;
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
-  if (dtype == 1)
-    hipLaunchKernelGGL((expert_wave_kernel<uint16_t, MODE, NT>), dim3(grid), dim3(XW_WAVES * WAVE), 0, s, a);
-  else
-    hipLaunchKernelGGL((expert_wave_kernel<float, MODE, NT>), dim3(grid), dim3(XW_WAVES * WAVE), 0, s, a);
+  const long long touched = n_groups < pairs ? n_groups : pairs;
+  return (pairs / 16 + touched) * s.n_tiles;
+}
+
+static size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+// One layout serves both halves (a caller may use a single buffer for the up
+// and the down launch in turn): counters for the larger item count of the
+// two, then the partial slots for the larger wave count.
+struct XWorkspace {
+  size_t ctr_bytes, part_bytes;
+};
+
+static XWorkspace x_workspace(int T, int kk, int n_groups, int H, int I, int dtype) {
+  XWorkspace w{};
+  long long items = 0, waves = 0;
+  for (int mode = XMODE_UP; mode <= XMODE_DOWN; ++mode) {
+    const XShape s = x_shape(mode, H, I, dtype);
+    const long long it = max_items(s, T, kk, n_groups);
+    long long wv = (it * s.nck + MIN_CPW - 1) / MIN_CPW;
+    if (wv > MAX_WAVES) wv = MAX_WAVES;
+    if (it > items) items = it;
+    if (wv > waves) waves = wv;
+  }
+  w.ctr_bytes = round256(static_cast<size_t>(items) * sizeof(int));
+  w.part_bytes = static_cast<size_t>(waves) * 2 * NT_MAX * WAVE * 4 * sizeof(float);
+  return w;
+}
+
+size_t expert_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dtype) {
+  if (T <= 0) return 0;
+  const XWorkspace w = x_workspace(T, kk, n_groups, H, I, dtype);
+  return w.ctr_bytes + w.part_bytes;
+}
+
+template <typename T, int MODE, int NT>
+static int resident_blocks() {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&expert_wave_kernel<T, MODE, NT>), XW_WAVES * WAVE, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  long long g = static_cast<long long>(device_cu_count()) * per_cu;
+  if (g * XW_WAVES > MAX_WAVES) g = MAX_WAVES / XW_WAVES;
+  return static_cast<int>(g);
+}
+
+template <typename T, int MODE, int NT>
+static void launch_t(XArgs a, hipStream_t s) {
+  const int grid = resident_blocks<T, MODE, NT>();
+  a.waves = grid * XW_WAVES;
+  hipLaunchKernelGGL((expert_wave_kernel<T, MODE, NT>), dim3(grid), dim3(XW_WAVES * WAVE), 0, s, a);
 }
 
 template <int MODE>
-static void launch_mode(int dtype, const XArgs& a, int T, int kk, hipStream_t s) {
-  if (pick_nt(T, kk, a.n_groups) == 1) launch_x<MODE, 1>(dtype, a, T, kk, s);
-  else launch_x<MODE, 2>(dtype, a, T, kk, s);
+static void launch_mode(int dtype, XArgs a, int T, int kk, void* ws, hipStream_t s) {
+  const XShape sh = x_shape(MODE, a.H, a.I_loc, dtype);
+  a.n_tiles = sh.n_tiles;
+  a.kfrag_total = sh.kfrag_total;
+  a.nck = sh.nck;
+  a.ctr = static_cast<int*>(ws);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                    x_workspace(T, kk, a.n_groups, a.H, a.I_loc, dtype).ctr_bytes);
+  const bool nt2 = pick_nt(T, kk, a.n_groups) == 2;
+  if (dtype == 1) {
+    if (nt2) launch_t<uint16_t, MODE, 2>(a, s);
+    else launch_t<uint16_t, MODE, 1>(a, s);
+  } else {
+    if (nt2) launch_t<float, MODE, 2>(a, s);
+    else launch_t<float, MODE, 1>(a, s);
+  }
 }
 
 void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, const int32_t* offsets,
-                      int n_groups, int T, int kk, const void* w13, int H, int I, void* A,
+                      int n_groups, int T, int kk, const void* w13, int H, int I, void* A, void* ws,
                       hipStream_t s) {
   XArgs a{};
   a.act = x;
@@ -341,13 +524,11 @@ void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, cons
   a.K = H;
   a.I_loc = I;
   a.H = H;
-  a.kfrag_total = H * elem_bytes_x(dtype) / FRAG_BYTES;
-  a.n_tiles = (I + 7) / 8;
-  launch_mode<XMODE_UP>(dtype, a, T, kk, s);
+  launch_mode<XMODE_UP>(dtype, a, T, kk, ws, s);
 }
 
 void launch_expert_down(int dtype, const void* A, const int32_t* offsets, int n_groups, int T,
-                        int kk, const void* w2, int H, int I, void* y_pair, hipStream_t s) {
+                        int kk, const void* w2, int H, int I, void* y_pair, void* ws, hipStream_t s) {
   XArgs a{};
   a.act = A;
   a.offsets = offsets;
@@ -358,9 +539,7 @@ void launch_expert_down(int dtype, const void* A, const int32_t* offsets, int n_
   a.K = I;
   a.I_loc = I;
   a.H = H;
-  a.kfrag_total = I * elem_bytes_x(dtype) / FRAG_BYTES;
-  a.n_tiles = (H + 15) / 16;
-  launch_mode<XMODE_DOWN>(dtype, a, T, kk, s);
+  launch_mode<XMODE_DOWN>(dtype, a, T, kk, ws, s);
 }
 
 }  // namespace moe

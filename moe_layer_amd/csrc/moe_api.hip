@@ -25,7 +25,7 @@ using namespace moe;
 
 namespace {
 
-constexpr int ABI_VERSION = 2;
+constexpr int ABI_VERSION = 3;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -69,11 +69,18 @@ const char* moe_status_str(int status) {
 }
 
 size_t moe_workspace_bytes(int op, int T, int kk, int n_groups, int H, int I, int dtype) {
-  (void)n_groups;
-  (void)H;
-  if (op != MOE_OP_GROUPED_GEMM || T <= 0 || kk <= 0 || I <= 0 || !dtype_ok(dtype)) return 0;
-  const size_t b = static_cast<size_t>(T) * kk * I * elem_bytes(dtype);
-  return (b + 255) & ~static_cast<size_t>(255);
+  if (T <= 0 || kk <= 0 || n_groups <= 0 || H <= 0 || I <= 0 || !dtype_ok(dtype)) return 0;
+  const size_t sk = expert_workspace_bytes(T, kk, n_groups, H, I, dtype);
+  switch (op) {
+    case MOE_OP_EXPERT_UP:
+    case MOE_OP_EXPERT_DOWN: return sk;
+    case MOE_OP_GROUPED_GEMM: {
+      // a, then the region both halves use in turn (each leaves its counters zero)
+      const size_t a = (static_cast<size_t>(T) * kk * I * elem_bytes(dtype) + 255) & ~static_cast<size_t>(255);
+      return a + sk;
+    }
+    default: return 0;
+  }
 }
 
 size_t moe_route_workspace_bytes(int T, int H, int E, int dtype) {
@@ -147,26 +154,32 @@ int moe_permute(const int32_t* topk_ids, int T, int kk, int g_begin, int n_group
 }
 
 int moe_expert_up(const void* x, const int32_t* sorted_pair, const int32_t* offsets, int T, int kk,
-                  int n_groups, const void* w13, int H, int I, int dtype, void* a,
-                  hipStream_t stream) {
+                  int n_groups, const void* w13, int H, int I, int dtype, void* a, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
   const int st = check_gemm_shapes(T, kk, n_groups, H, I, dtype);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!x || !sorted_pair || !offsets || !w13 || !a) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(w13) || !aligned16(a) || !aligned4(sorted_pair) || !aligned4(offsets))
     return MOE_EINVAL;
-  launch_expert_up(dtype, x, sorted_pair, offsets, n_groups, T, kk, w13, H, I, a, stream);
+  if (!ws || !aligned16(ws) || ws_bytes < moe_workspace_bytes(MOE_OP_EXPERT_UP, T, kk, n_groups, H, I, dtype))
+    return MOE_EWORKSPACE;
+  launch_expert_up(dtype, x, sorted_pair, offsets, n_groups, T, kk, w13, H, I, a, ws, stream);
   return launched();
 }
 
 int moe_expert_down(const void* a, const int32_t* offsets, int T, int kk, int n_groups,
-                    const void* w2, int H, int I, int dtype, void* y_pair, hipStream_t stream) {
+                    const void* w2, int H, int I, int dtype, void* y_pair, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
   const int st = check_gemm_shapes(T, kk, n_groups, H, I, dtype);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!a || !offsets || !w2 || !y_pair) return MOE_EINVAL;
   if (!aligned16(a) || !aligned16(w2) || !aligned16(y_pair) || !aligned4(offsets)) return MOE_EINVAL;
-  launch_expert_down(dtype, a, offsets, n_groups, T, kk, w2, H, I, y_pair, stream);
+  if (!ws || !aligned16(ws) ||
+      ws_bytes < moe_workspace_bytes(MOE_OP_EXPERT_DOWN, T, kk, n_groups, H, I, dtype))
+    return MOE_EWORKSPACE;
+  launch_expert_down(dtype, a, offsets, n_groups, T, kk, w2, H, I, y_pair, ws, stream);
   return launched();
 }
 
@@ -182,8 +195,10 @@ int moe_grouped_gemm(const void* x, const int32_t* sorted_pair, const int32_t* o
     return MOE_EINVAL;
   if (!ws || !aligned16(ws) || ws_bytes < moe_workspace_bytes(MOE_OP_GROUPED_GEMM, T, kk, n_groups, H, I, dtype))
     return MOE_EWORKSPACE;
-  launch_expert_up(dtype, x, sorted_pair, offsets, n_groups, T, kk, w13, H, I, ws, stream);
-  launch_expert_down(dtype, ws, offsets, n_groups, T, kk, w2, H, I, y_pair, stream);
+  const size_t a_bytes = (static_cast<size_t>(T) * kk * I * elem_bytes(dtype) + 255) & ~static_cast<size_t>(255);
+  void* sk = static_cast<char*>(ws) + a_bytes;
+  launch_expert_up(dtype, x, sorted_pair, offsets, n_groups, T, kk, w13, H, I, ws, sk, stream);
+  launch_expert_down(dtype, ws, offsets, n_groups, T, kk, w2, H, I, y_pair, sk, stream);
   return launched();
 }
 

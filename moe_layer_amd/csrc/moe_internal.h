@@ -30,13 +30,16 @@ void launch_route(int dtype, const void* x, const void* wg, const float* bias, f
 // counts, offsets, stable permutation
 void launch_permute(const int32_t* ids, int T, int kk, int g_begin, int n_groups, int32_t* counts,
                     int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s);
+// expert GEMM workspace (one layout for the up and the down launch): split-item
+// counters + per-wave partials
+size_t expert_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dtype);
 // expert up-projection with SiLU(gate)*up epilogue -> A (n_pairs, I)
 void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, const int32_t* offsets,
-                      int n_groups, int T, int kk, const void* w13, int H, int I, void* a,
+                      int n_groups, int T, int kk, const void* w13, int H, int I, void* a, void* ws,
                       hipStream_t s);
 // expert down-projection -> y_pair (n_pairs, H)
 void launch_expert_down(int dtype, const void* a, const int32_t* offsets, int n_groups, int T,
-                        int kk, const void* w2, int H, int I, void* y_pair, hipStream_t s);
+                        int kk, const void* w2, int H, int I, void* y_pair, void* ws, hipStream_t s);
 // weighted combine -> y (T, H)
 void launch_combine(int dtype, const void* y_pair, const int32_t* pair_pos, const float* w, int T,
                     int kk, int H, void* y, hipStream_t s);

@@ -29,6 +29,7 @@ class MoeLayerBuffers:
     y_pair: torch.Tensor
     y: torch.Tensor
     route_ws: torch.Tensor
+    expert_ws: torch.Tensor
 
     @classmethod
     def allocate(cls, T, H, E, kk, n_groups, I, dtype, device="cuda"):
@@ -48,6 +49,7 @@ class MoeLayerBuffers:
             y_pair=torch.empty((T * kk, H), **act),
             y=torch.empty((T, H), **act),
             route_ws=_lib.route_workspace(T, H, E, dtype, dev),
+            expert_ws=_lib.expert_workspace(T, kk, n_groups, H, I, dtype, dev),
         )
 
 
@@ -75,7 +77,7 @@ def moe_layer_forward(x, w_gate, gate_bias, w13, w2, k, renorm, n_shared=0, g_be
                        bufs.topk_w, bufs.route_ws, stream)
         _lib.moe_permute(bufs.topk_ids, g_begin, G, bufs.counts, bufs.offsets, bufs.sorted_pair,
                          bufs.pair_pos, stream)
-    _lib.moe_expert_up(x, bufs.sorted_pair, bufs.offsets, kk, w13, bufs.a, stream)
-    _lib.moe_expert_down(bufs.a, bufs.offsets, T, kk, w2, bufs.y_pair, stream)
+    _lib.moe_expert_up(x, bufs.sorted_pair, bufs.offsets, kk, w13, bufs.a, bufs.expert_ws, stream)
+    _lib.moe_expert_down(bufs.a, bufs.offsets, T, kk, w2, bufs.y_pair, bufs.expert_ws, stream)
     _lib.moe_combine(bufs.y_pair, bufs.pair_pos, bufs.topk_w, bufs.y, stream)
     return bufs

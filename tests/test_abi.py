@@ -43,7 +43,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     for s in range(5):
         assert L.moe_status_str(s).decode().startswith(
             ["MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP"][s])
@@ -51,10 +51,20 @@ def test_version_and_status_strings(L):
 
 
 def test_workspace_size(L):
-    assert L.moe_workspace_bytes(2, 256, 8, 66, 2048, 1408, BF16) == 256 * 8 * 1408 * 2
-    assert L.moe_workspace_bytes(2, 3, 3, 4, 256, 40, F32) == 1536  # 3*3*40*4 = 1440, rounded up to 256
+    up = L.moe_workspace_bytes(5, 256, 8, 66, 2048, 1408, BF16)
+    down = L.moe_workspace_bytes(6, 256, 8, 66, 2048, 1408, BF16)
+    a = 256 * 8 * 1408 * 2
+    assert up > 0 and up == down and up % 256 == 0  # one layout serves both halves
+    assert L.moe_workspace_bytes(2, 256, 8, 66, 2048, 1408, BF16) == a + up
+    # a of 3*3*40*4 = 1440 bytes is padded to 1536 before the split-item region
+    assert L.moe_workspace_bytes(2, 3, 3, 4, 256, 40, F32) == 1536 + L.moe_workspace_bytes(
+        5, 3, 3, 4, 256, 40, F32)
     assert L.moe_workspace_bytes(0, 256, 8, 66, 2048, 1408, BF16) == 0
     assert L.moe_workspace_bytes(2, 0, 8, 66, 2048, 1408, BF16) == 0
+    assert L.moe_workspace_bytes(5, 256, 8, 0, 2048, 1408, BF16) == 0
+    # grows with the batch, independent of the device
+    assert L.moe_workspace_bytes(5, 2048, 8, 16, 4096, 1536, BF16) > L.moe_workspace_bytes(
+        5, 8, 8, 16, 4096, 1536, BF16)
 
 
 def route(L, x=FAKE, wg=FAKE, b=None, T=4, H=256, E=8, k=2, renorm=1, ns=0, dt=BF16,
@@ -154,8 +164,16 @@ def test_grouped_gemm_rejects(L, kw, status):
 
 
 def test_expert_halves_reject(L):
-    assert L.moe_expert_up(FAKE, FAKE, FAKE, 4, 2, 8, FAKE, 256, 128, BF16, None, None) == MOE_EINVAL
-    assert L.moe_expert_down(FAKE, FAKE, 4, 2, 8, FAKE, 256, 100, BF16, FAKE, None) == MOE_EUNSUPPORTED
+    up = lambda **kw: L.moe_expert_up(FAKE, FAKE, FAKE, 4, 2, 8, FAKE, 256, 128, BF16, kw.get("a", FAKE),
+                                      kw.get("ws", FAKE), kw.get("ws_bytes", 1 << 30), None)
+    assert up(a=None) == MOE_EINVAL
+    assert up(ws=None) == MOE_EWORKSPACE
+    assert up(ws=MISALIGNED) == MOE_EWORKSPACE
+    assert up(ws_bytes=16) == MOE_EWORKSPACE
+    assert L.moe_expert_down(FAKE, FAKE, 4, 2, 8, FAKE, 256, 100, BF16, FAKE, FAKE, 1 << 30,
+                             None) == MOE_EUNSUPPORTED
+    assert L.moe_expert_down(FAKE, FAKE, 4, 2, 8, FAKE, 256, 128, BF16, FAKE, None, 1 << 30,
+                             None) == MOE_EWORKSPACE
 
 
 def test_combine_rejects(L):

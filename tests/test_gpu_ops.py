@@ -300,3 +300,34 @@ def test_route_workspace_reused_across_shapes():
         c, o, sp, pos = oracle.permute(ids_ref, 0, cfg.E)
         assert np.array_equal(gh.from_dev(bufs.offsets), o)
         assert np.array_equal(gh.from_dev(bufs.sorted_pair)[: o[-1]], sp)
+
+
+@pytest.mark.gpu
+def test_expert_workspace_reused_across_shapes():
+    """The expert GEMMs split items along K over waves; the split-item
+    counters come back to zero after every call, so one workspace serves
+    calls of different batch sizes in turn with bit-identical results."""
+    import torch
+
+    import gpu_helpers as gh
+    import moe_layer_amd
+    cfg = small(H=2048, E=16, k=4, I=256, T=200)
+    d = make_layer_inputs(cfg, 200, seed=21)
+    wg, b = gh.to_dev(d["w_gate"]), gh.to_dev(d["gate_bias"])
+    w13, w2 = gh.to_dev(d["w13"]), gh.to_dev(d["w2"])
+    shared = moe_layer_amd.expert_workspace(200, cfg.k, cfg.E, cfg.H, cfg.I, torch.bfloat16)
+    print("[case] expert workspace reuse", flush=True)
+    for T in (200, 3, 64, 200):
+        x = gh.to_dev(d["x"][:T])
+        outs = []
+        for ws in (shared, moe_layer_amd.expert_workspace(T, cfg.k, cfg.E, cfg.H, cfg.I, torch.bfloat16)):
+            bufs = moe_layer_amd.MoeLayerBuffers.allocate(T, cfg.H, cfg.E, cfg.k, cfg.E, cfg.I, torch.bfloat16)
+            moe_layer_amd.moe_route_permute(x, wg, b, cfg.k, True, 0, bufs.logits, bufs.topk_ids,
+                                            bufs.topk_w, 0, cfg.E, bufs.counts, bufs.offsets,
+                                            bufs.sorted_pair, bufs.pair_pos, bufs.route_ws)
+            moe_layer_amd.moe_expert_up(x, bufs.sorted_pair, bufs.offsets, cfg.k, w13, bufs.a, ws)
+            moe_layer_amd.moe_expert_down(bufs.a, bufs.offsets, T, cfg.k, w2, bufs.y_pair, ws)
+            torch.cuda.synchronize()
+            n = int(gh.from_dev(bufs.offsets)[-1])
+            outs.append((gh.from_dev(bufs.a)[:n].copy(), gh.from_dev(bufs.y_pair)[:n].copy()))
+        assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1]), T
