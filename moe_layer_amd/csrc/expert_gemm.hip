@@ -8,7 +8,9 @@
 // Decode-shaped problems are HBM-bound: every weight byte must stream from
 // HBM exactly once while the token side (a few to a few dozen rows per
 // expert) is small and stays in L2.  Work item = (group g, tile of 16 weight
-// rows, pass of up to 16*NT token rows), over the full K:
+// rows, pass of 16 token rows -- 32 in the two-tile kernel when the group has
+// more than 16), over the full K; a group's items run tile-major, so the
+// passes over one weight tile are adjacent:
 //   up   : the 16 rows are 8 gate rows and the matching 8 up rows, so
 //          SiLU(gate)*up is formed in registers;
 //   down : 16 rows of W2 = 16 output features.
@@ -74,22 +76,35 @@ struct XArgs {
   float* part;             // per-wave partial tiles: [wave][2][NT][64 lanes][4]
 };
 
-// Wave 0: s_off[g] = offsets[g]; s_pstart[g] = number of mp-row passes of the
-// groups before g; s_pstart[n_groups] = total passes.
-__device__ __forceinline__ void pass_prefix(const int* __restrict__ offsets, int n_groups, int mp,
-                                            int* s_pstart, int* s_off) {
+// Token rows per pass of a group with m rows: 16, or 32 when the kernel
+// holds two token tiles and the group has more than 16 rows.
+template <int NT>
+__device__ __forceinline__ int pass_rows(int m) {
+  return (NT == 2 && m > 16) ? 32 : 16;
+}
+
+// Wave 0: s_off[g] = offsets[g]; s_istart[g] = items of the groups before g
+// (passes x weight tiles each); s_istart[n_groups] = total items.
+template <int NT>
+__device__ __forceinline__ void item_prefix(const int* __restrict__ offsets, int n_groups, int n_tiles,
+                                            int* s_istart, int* s_off) {
   if (threadIdx.x >= WAVE) return;
   const int l = lane_id();
   int base = 0;
   for (int g0 = 0; g0 <= n_groups; g0 += WAVE) {
     const int g = g0 + l;
     if (g <= n_groups) s_off[g] = offsets[g];
-    const int v = (g < n_groups) ? (offsets[g + 1] - offsets[g] + mp - 1) / mp : 0;
+    int v = 0;
+    if (g < n_groups) {
+      const int m = offsets[g + 1] - offsets[g];
+      const int ps = pass_rows<NT>(m);
+      v = (m + ps - 1) / ps * n_tiles;
+    }
     const int incl = wave_inclusive_scan(v);
-    if (g < n_groups) s_pstart[g] = base + incl - v;
+    if (g < n_groups) s_istart[g] = base + incl - v;
     base += __shfl(incl, WAVE - 1, WAVE);
   }
-  if (l == 0) s_pstart[n_groups] = base;
+  if (l == 0) s_istart[n_groups] = base;
 }
 
 __device__ __forceinline__ uint4 ld16_nt(const char* p) {
@@ -99,7 +114,7 @@ __device__ __forceinline__ uint4 ld16_nt(const char* p) {
 
 template <int NT>
 struct WItem {
-  int row0, m, t0, n0;     // group's first sorted row, its row count, pass start, first weight row
+  int row0, m_end, t0, n0; // group's first sorted row, end of this pass's rows, pass start, first weight row
   const char* wp[4];       // rows 4j + l/16 (j = 0..3) of the item's 16, + 16*(l%16)
   int tok[NT];             // activation row of this lane's token in each 16-row tile
 };
@@ -108,20 +123,25 @@ struct WItem {
 // (needs only the pass table, so the first weight loads can be issued before
 // any token index is known).
 template <typename T, int MODE, int NT>
-__device__ __forceinline__ void witem_weights(const XArgs& a, const int* s_pstart, const int* s_off,
+__device__ __forceinline__ void witem_weights(const XArgs& a, const int* s_istart, const int* s_off,
                                               int item, int lrow, int lq, size_t row_bytes,
                                               WItem<NT>& it) {
-  const int pi = item / a.n_tiles;
-  const int nt = item % a.n_tiles;
-  int lo = 0, hi = a.n_groups;  // s_pstart[lo] <= pi < s_pstart[hi]
+  int lo = 0, hi = a.n_groups;  // s_istart[lo] <= item < s_istart[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (s_pstart[mid] <= pi) lo = mid;
+    if (s_istart[mid] <= item) lo = mid;
     else hi = mid;
   }
+  // Within a group, items go tile-major: the passes over one weight tile are
+  // adjacent, so its re-reads follow right behind the first read.
   it.row0 = s_off[lo];
-  it.m = s_off[lo + 1] - it.row0;
-  it.t0 = (pi - s_pstart[lo]) * (16 * NT);
+  const int m = s_off[lo + 1] - it.row0;
+  const int ps = pass_rows<NT>(m);
+  const int np = (m + ps - 1) / ps;
+  const int local = item - s_istart[lo];
+  const int nt = local / np;
+  it.t0 = (local - nt * np) * ps;
+  it.m_end = min(m, it.t0 + ps);
   // Item row i (0..15) is, for up, gate row n0 + i (i < 8) or up row
   // I' + n0 + i - 8; for down, W2 row n0 + i.  Rows past the matrix are
   // clamped (read, never stored).
@@ -146,16 +166,16 @@ template <typename T, int MODE, int NT>
 __device__ __forceinline__ void witem_tokens(const XArgs& a, int lrow, WItem<NT>& it) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
-    const int r = it.row0 + min(it.t0 + tt * 16 + lrow, it.m - 1);
+    const int r = it.row0 + min(it.t0 + tt * 16 + lrow, it.m_end - 1);
     it.tok[tt] = (MODE == XMODE_UP) ? a.sorted_pair[r] / a.kk : r;
   }
 }
 
 template <typename T, int MODE, int NT>
-__device__ __forceinline__ void witem_setup(const XArgs& a, const int* s_pstart, const int* s_off,
+__device__ __forceinline__ void witem_setup(const XArgs& a, const int* s_istart, const int* s_off,
                                             int item, int lrow, int lq, size_t row_bytes,
                                             WItem<NT>& it) {
-  witem_weights<T, MODE, NT>(a, s_pstart, s_off, item, lrow, lq, row_bytes, it);
+  witem_weights<T, MODE, NT>(a, s_istart, s_off, item, lrow, lq, row_bytes, it);
   witem_tokens<T, MODE, NT>(a, lrow, it);
 }
 
@@ -209,7 +229,9 @@ __device__ __forceinline__ void wtranspose(const uint4 (&w)[CHUNK_FRAGS], char* 
 }
 
 // Fragments f >= nf lie past the end of K: their token side is zeroed here,
-// so they add exactly nothing whatever the weight side holds.
+// so they add exactly nothing whatever the weight side holds.  A tile past
+// the pass's rows (repeated rows) is multiplied too -- branching around it
+// costs more than the MFMAs -- and never stored.
 template <typename T, int NT>
 __device__ __forceinline__ void wmma(const uint4 (&w)[CHUNK_FRAGS], const uint4 (&x)[NT][CHUNK_FRAGS],
                                      int nf, f32x4_t (&acc)[NT]) {
@@ -231,7 +253,7 @@ __device__ __forceinline__ void wstore(const XArgs& a, const WItem<NT>& it, f32x
 #pragma unroll
       for (int r = 0; r < 4; ++r) up[r] = __shfl_xor(acc[tt][r], 32, WAVE);
       const int n = it.n0 + 4 * lq;
-      if (lq < 2 && tr < it.m && n < a.I_loc) {
+      if (lq < 2 && tr < it.m_end && n < a.I_loc) {
         float o[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -243,7 +265,7 @@ __device__ __forceinline__ void wstore(const XArgs& a, const WItem<NT>& it, f32x
       }
     } else {
       const int n = it.n0 + 4 * lq;
-      if (tr < it.m && n < a.H) {
+      if (tr < it.m_end && n < a.H) {
         T* dst = reinterpret_cast<T*>(a.out) + static_cast<size_t>(it.row0 + tr) * a.H + n;
         Elem<T>::store4(dst, acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
       }
@@ -316,7 +338,7 @@ __device__ __forceinline__ void finish_split(const XArgs& a, const WItem<NT>& it
 
 template <typename T, int MODE, int NT>
 __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
-  __shared__ int s_pstart[MAX_GROUPS + 1];
+  __shared__ int s_istart[MAX_GROUPS + 1];
   __shared__ int s_off[MAX_GROUPS + 1];
   __shared__ __attribute__((aligned(16))) char s_wt[XW_WAVES][16 * WT_ROW];
 
@@ -325,9 +347,9 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   const int lrow = l & 15;
   const int lq = l >> 4;
 
-  pass_prefix(a.offsets, a.n_groups, 16 * NT, s_pstart, s_off);
+  item_prefix<NT>(a.offsets, a.n_groups, a.n_tiles, s_istart, s_off);
   __syncthreads();  // the only barrier; waves are independent from here on
-  const long long Q = static_cast<long long>(s_pstart[a.n_groups]) * a.n_tiles * a.nck;
+  const long long Q = static_cast<long long>(s_istart[a.n_groups]) * a.nck;
   const int W = static_cast<int>(min(static_cast<long long>(a.waves), (Q + MIN_CPW - 1) / MIN_CPW));
   const int w = wv * gridDim.x + blockIdx.x;
   if (w >= W) return;  // wave-uniform
@@ -343,13 +365,13 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   int ce = static_cast<int>(min(static_cast<long long>(a.nck), q1 - static_cast<long long>(item) * a.nck));
   // The first weight chunk goes out before the token indices are fetched.
   WItem<NT> cur, nxt;
-  witem_weights<T, MODE, NT>(a, s_pstart, s_off, item, lrow, lq, row_bytes, cur);
+  witem_weights<T, MODE, NT>(a, s_istart, s_off, item, lrow, lq, row_bytes, cur);
   uint4 w0[CHUNK_FRAGS], w1[CHUNK_FRAGS], x[NT][CHUNK_FRAGS];
   int c = cb;
   wload(cur.wp, c, a.kfrag_total, lrow, w0);
   witem_tokens<T, MODE, NT>(a, lrow, cur);
   bool have_nxt = static_cast<long long>(item + 1) * a.nck < q1;
-  if (have_nxt) witem_setup<T, MODE, NT>(a, s_pstart, s_off, item + 1, lrow, lq, row_bytes, nxt);
+  if (have_nxt) witem_setup<T, MODE, NT>(a, s_istart, s_off, item + 1, lrow, lq, row_bytes, nxt);
 
   f32x4_t acc[NT];
 #pragma unroll
@@ -394,7 +416,7 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
       ce = static_cast<int>(min(static_cast<long long>(a.nck), q1 - static_cast<long long>(item) * a.nck)); \
       have_nxt = static_cast<long long>(item + 1) * a.nck < q1;                           \
       if (have_nxt)                                                                       \
-        witem_setup<T, MODE, NT>(a, s_pstart, s_off, item + 1, lrow, lq, row_bytes, nxt);  \
+        witem_setup<T, MODE, NT>(a, s_istart, s_off, item + 1, lrow, lq, row_bytes, nxt);  \
     }                                                                                     \
   }
 
@@ -409,8 +431,9 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
 
 static int elem_bytes_x(int dtype) { return dtype == 1 ? 2 : 4; }
 
-// Token rows per pass (16 * NT) from the mean rows per group (exact for the
-// full and TP views; an over-estimate for an EP share).
+// Two token tiles from the mean rows per group (exact for the full and TP
+// views; an over-estimate for an EP share).  In that kernel a group with at
+// most 16 rows still runs one 16-row pass.
 static int pick_nt(int T, int kk, int n_groups) {
   const double mean = static_cast<double>(T) * kk / n_groups;
   return (mean > 12.0 && T > 16) ? 2 : 1;
@@ -460,6 +483,12 @@ static XWorkspace x_workspace(int T, int kk, int n_groups, int H, int I, int dty
   w.ctr_bytes = round256(static_cast<size_t>(items) * sizeof(int));
   w.part_bytes = static_cast<size_t>(waves) * 2 * NT_MAX * WAVE * 4 * sizeof(float);
   return w;
+}
+
+bool expert_items_fit(int T, int kk, int n_groups, int H, int I, int dtype) {
+  for (int mode = XMODE_UP; mode <= XMODE_DOWN; ++mode)
+    if (max_items(x_shape(mode, H, I, dtype), T, kk, n_groups) > 0x7fffffffLL) return false;
+  return true;
 }
 
 size_t expert_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dtype) {

@@ -48,6 +48,7 @@ int check_gemm_shapes(int T, int kk, int n_groups, int H, int I, int dtype) {
   if (!k_len_ok(H, dtype) || H % 16 != 0) return MOE_EUNSUPPORTED;
   if (!k_len_ok(I, dtype) || I % 8 != 0) return MOE_EUNSUPPORTED;
   if (static_cast<long long>(T) * kk > (1LL << 30)) return MOE_EUNSUPPORTED;
+  if (!expert_items_fit(T, kk, n_groups, H, I, dtype)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 

@@ -33,6 +33,8 @@ void launch_permute(const int32_t* ids, int T, int kk, int g_begin, int n_groups
 // expert GEMM workspace (one layout for the up and the down launch): split-item
 // counters + per-wave partials
 size_t expert_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dtype);
+// whether every work item of these sizes has a 32-bit index
+bool expert_items_fit(int T, int kk, int n_groups, int H, int I, int dtype);
 // expert up-projection with SiLU(gate)*up epilogue -> A (n_pairs, I)
 void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, const int32_t* offsets,
                       int n_groups, int T, int kk, const void* w13, int H, int I, void* a, void* ws,
