@@ -7,14 +7,24 @@
 //
 // Decode-shaped problems are HBM-bound: every weight byte must stream from
 // HBM exactly once while the token side (a few to a few dozen rows per
-// expert) is small and stays in L2.  Work item = (group g, tile of 16 weight
-// rows, pass of 16 token rows -- 32 in the two-tile kernel when the group has
-// more than 16), over the full K; a group's items run tile-major, so the
-// passes over one weight tile are adjacent:
-//   up   : the 16 rows are 8 gate rows and the matching 8 up rows, so
-//          SiLU(gate)*up is formed in registers;
+// expert) is small and stays in L2.
+//
+// Work item = (group g, SUB adjacent weight tiles (1 or 4, per launch), pass
+// of 16 token rows -- 32 in the two-tile kernel when the group has more than
+// 16) over the full K.  A weight tile is 16 rows:
+//   up   : 8 gate rows and the matching 8 up rows, so SiLU(gate)*up is
+//          formed in registers;
 //   down : 16 rows of W2 = 16 output features.
-// K is walked in 512-byte chunks.
+// K is walked in 512-byte chunks; for each chunk the wave loads the token
+// fragments once and multiplies them against the chunk of each of the item's
+// tiles in turn, so with four tiles every token byte fetched serves four
+// times as many weight bytes (with a few dozen tokens per expert their rows
+// no longer fit L1, and these L2 reads otherwise crowd out the weight
+// stream); four tiles also keep very short rows (small K) from making items
+// too small.  With few tokens, one tile keeps items fine-grained.  A group's
+// items run tile-major, so the passes over one set of tiles are adjacent.
+// Tiles of the last item past the matrix alias tile 0 (read, never stored),
+// so every step issues the same loads.
 //
 // Balance.  With every CU streaming, one CU moves only ~1/256 of the chip's
 // HBM bandwidth, so the launch lasts as long as its most loaded CU.  The
@@ -22,7 +32,7 @@
 // flattened sequence of (item, chunk) is cut into equal contiguous ranges,
 // one per wave (wave w = wv * grid + block, so a partly used grid still
 // covers every CU).  An item whose chunks fall into several waves' ranges is
-// split along K: each of those waves stores its fp32 partial tile, and the
+// split along K: each of those waves stores its fp32 partial tiles, and the
 // last of them to arrive (an integer counter per item; nobody waits) adds the
 // partials in K order and runs the epilogue.  The sum order depends only on
 // the shapes and the grid, so results are reproducible.  Waves are otherwise
@@ -31,18 +41,20 @@
 //
 // Weights are read DRAM-friendly: each load instruction takes 256 contiguous
 // bytes from each of 4 rows (non-temporal, streamed once), double-buffered in
-// registers so chunk c+1 is in flight while chunk c is multiplied.  The wave
-// then passes its 16 rows x 512 B through a private LDS tile (rows padded by
-// 16 B) to read them back in the 16x16 MFMA operand layout (lane l: row
-// l%16, bytes 16*(l/16) of each 64-byte fragment); only the wave itself
-// touches that tile, so no barrier is needed.  Token fragments of chunk c
-// come from L2 just before use and are issued ahead of the next weight chunk,
-// so waiting for them (loads retire in order) never waits for the weights in
-// flight.  The stream runs across item boundaries, and the next item's
-// token-row indices are fetched one item ahead.  Token rows past the group's
-// count repeat a real row and are never stored; fragments past the end of K
-// are zero on both sides.  Every output element is written by exactly one
-// lane.
+// registers so the next tile-chunk is in flight while the current one is
+// multiplied.  The wave passes each 16 rows x 512 B through a private LDS
+// tile (rows padded by 16 B) to read them back in the 16x16 MFMA operand
+// layout (lane l: row l%16, bytes 16*(l/16) of each 64-byte fragment); only
+// the wave itself touches that tile, so no barrier is needed.  Token
+// fragments of a chunk come from L2 just before use and are issued ahead of
+// the next weight load, so waiting for them (loads retire in order) never
+// waits for the weights in flight.  All addresses are a wave-uniform base
+// plus a 32-bit lane offset (scalar-base loads, constant offsets folded into
+// the instructions).  The stream runs across item boundaries, and the next
+// item's token-row indices are fetched one item ahead.  Token rows past the
+// group's count repeat a real row and are never stored; fragments past the
+// end of K are zero on both sides.  Every output element is written by
+// exactly one lane.
 #include "common.hpp"
 #include "moe_internal.h"
 
@@ -51,7 +63,8 @@ namespace moe {
 constexpr int XW_WAVES = 4;                             // waves per block (independent)
 constexpr int CHUNK_FRAGS = 8;                          // 64-byte fragments per chunk
 constexpr int CHUNK_BYTES = CHUNK_FRAGS * FRAG_BYTES;   // 512
-constexpr int MIN_CPW = 4;                              // chunks per wave at least (bounds split items)
+constexpr int SUB_MAX = 4;                              // weight tiles per item at most
+constexpr int MIN_CPW = 2;                              // chunks per wave at least (bounds split items)
 constexpr int MAX_WAVES = 4096;                         // waves of one launch at most
 constexpr int NT_MAX = 2;
 
@@ -70,10 +83,11 @@ struct XArgs {
   int H;
   int kfrag_total;         // K * elem / 64
   int n_tiles;             // 16-row weight tiles per group
+  int n_quads;             // items per pass: ceil(n_tiles / SUB) (SUB = weight tiles per item)
   int nck;                 // 512-byte chunks per item
   int waves;               // waves launched
   int* ctr;                // per-item arrival counters (zero between calls)
-  float* part;             // per-wave partial tiles: [wave][2][NT][64 lanes][4]
+  float* part;             // per-wave partial tiles: [wave][2][SUB][NT][64 lanes][4]
 };
 
 // Token rows per pass of a group with m rows: 16, or 32 when the kernel
@@ -84,9 +98,9 @@ __device__ __forceinline__ int pass_rows(int m) {
 }
 
 // Wave 0: s_off[g] = offsets[g]; s_istart[g] = items of the groups before g
-// (passes x weight tiles each); s_istart[n_groups] = total items.
+// (passes x quads each); s_istart[n_groups] = total items.
 template <int NT>
-__device__ __forceinline__ void item_prefix(const int* __restrict__ offsets, int n_groups, int n_tiles,
+__device__ __forceinline__ void item_prefix(const int* __restrict__ offsets, int n_groups, int n_quads,
                                             int* s_istart, int* s_off) {
   if (threadIdx.x >= WAVE) return;
   const int l = lane_id();
@@ -98,7 +112,7 @@ __device__ __forceinline__ void item_prefix(const int* __restrict__ offsets, int
     if (g < n_groups) {
       const int m = offsets[g + 1] - offsets[g];
       const int ps = pass_rows<NT>(m);
-      v = (m + ps - 1) / ps * n_tiles;
+      v = (m + ps - 1) / ps * n_quads;
     }
     const int incl = wave_inclusive_scan(v);
     if (g < n_groups) s_istart[g] = base + incl - v;
@@ -107,111 +121,146 @@ __device__ __forceinline__ void item_prefix(const int* __restrict__ offsets, int
   if (l == 0) s_istart[n_groups] = base;
 }
 
-__device__ __forceinline__ uint4 ld16_nt(const char* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+// Loads from a wave-uniform base (kept in SGPRs) plus a 32-bit lane offset:
+// the compiler emits global_load with a scalar base and folds constant
+// offsets into the instruction, so no per-lane 64-bit address arithmetic is
+// spent per load.
+__device__ __forceinline__ uint4 ldg_nt(const char* base, uint32_t off) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + off));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint4 ldg(const char* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(base + off);
+}
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 template <int NT>
 struct WItem {
   int row0, m_end, t0, n0; // group's first sorted row, end of this pass's rows, pass start, first weight row
-  const char* wp[4];       // rows 4j + l/16 (j = 0..3) of the item's 16, + 16*(l%16)
-  int tok[NT];             // activation row of this lane's token in each 16-row tile
+  int n_sub;               // tiles of the item inside the matrix (1..SUB)
+  const char* wbase;       // the item's first weight row (wave-uniform)
+  uint32_t sub_bytes;      // byte distance between consecutive tiles of the item
+  uint32_t woff[4];        // lane: row 4j + lq of a tile, + 16*lrow, relative to the tile's base
+  uint32_t xoff[NT];       // lane: its token's activation row, + 16*lq, relative to the activations
 };
 
-// Weight side of an item: group, row window and the lane's 4 row pointers
-// (needs only the pass table, so the first weight loads can be issued before
-// any token index is known).
-template <typename T, int MODE, int NT>
+// Weight side of an item: group, row window and the lane's 4 row offsets
+// (needs only the item table, so the first weight loads can be issued before
+// any token index is known).  `item` is wave-uniform.
+template <typename T, int MODE, int NT, int SUB>
 __device__ __forceinline__ void witem_weights(const XArgs& a, const int* s_istart, const int* s_off,
-                                              int item, int lrow, int lq, size_t row_bytes,
+                                              int item, int lrow, int lq, uint32_t row_bytes,
                                               WItem<NT>& it) {
   int lo = 0, hi = a.n_groups;  // s_istart[lo] <= item < s_istart[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (s_istart[mid] <= item) lo = mid;
+    if (uni(s_istart[mid]) <= item) lo = mid;
     else hi = mid;
   }
-  // Within a group, items go tile-major: the passes over one weight tile are
-  // adjacent, so its re-reads follow right behind the first read.
-  it.row0 = s_off[lo];
-  const int m = s_off[lo + 1] - it.row0;
+  it.row0 = uni(s_off[lo]);
+  const int m = uni(s_off[lo + 1]) - it.row0;
   const int ps = pass_rows<NT>(m);
   const int np = (m + ps - 1) / ps;
-  const int local = item - s_istart[lo];
-  const int nt = local / np;
-  it.t0 = (local - nt * np) * ps;
+  const int local = item - uni(s_istart[lo]);
+  const int nq = local / np;
+  it.t0 = (local - nq * np) * ps;
   it.m_end = min(m, it.t0 + ps);
-  // Item row i (0..15) is, for up, gate row n0 + i (i < 8) or up row
-  // I' + n0 + i - 8; for down, W2 row n0 + i.  Rows past the matrix are
-  // clamped (read, never stored).
+  it.n_sub = min(SUB, a.n_tiles - nq * SUB);
+  // Tile s of the quad, row i (0..15): for up, gate row n0 + 8s + i (i < 8)
+  // or up row I' + n0 + 8s + i - 8; for down, W2 row n0 + 16s + i.  I' is a
+  // multiple of 8 and H of 16, so every tile is whole.
+  size_t first_row;
+  if (MODE == XMODE_UP) {
+    it.n0 = nq * SUB * 8;
+    first_row = static_cast<size_t>(lo) * (2 * a.I_loc) + it.n0;
+    it.sub_bytes = 8 * row_bytes;
+  } else {
+    it.n0 = nq * SUB * 16;
+    first_row = static_cast<size_t>(lo) * a.H + it.n0;
+    it.sub_bytes = 16 * row_bytes;
+  }
+  it.wbase = reinterpret_cast<const char*>(a.w) + first_row * row_bytes;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = 4 * j + lq;
-    size_t wrow;
-    if (MODE == XMODE_UP) {
-      it.n0 = nt * 8;
-      const int n = min(it.n0 + (i & 7), a.I_loc - 1);
-      wrow = static_cast<size_t>(lo) * (2 * a.I_loc) + (i < 8 ? n : a.I_loc + n);
-    } else {
-      it.n0 = nt * 16;
-      wrow = static_cast<size_t>(lo) * a.H + min(it.n0 + i, a.H - 1);
-    }
-    it.wp[j] = reinterpret_cast<const char*>(a.w) + wrow * row_bytes + lrow * 16;
+    const int rel = (MODE == XMODE_UP) ? (i < 8 ? i : a.I_loc + i - 8) : i;
+    it.woff[j] = static_cast<uint32_t>(rel) * row_bytes + 16 * lrow;
   }
 }
 
 // Token side: the activation row of this lane's token in each 16-row tile.
 template <typename T, int MODE, int NT>
-__device__ __forceinline__ void witem_tokens(const XArgs& a, int lrow, WItem<NT>& it) {
+__device__ __forceinline__ void witem_tokens(const XArgs& a, int lrow, int lq, uint32_t row_bytes,
+                                             WItem<NT>& it) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     const int r = it.row0 + min(it.t0 + tt * 16 + lrow, it.m_end - 1);
-    it.tok[tt] = (MODE == XMODE_UP) ? a.sorted_pair[r] / a.kk : r;
+    const int tok = (MODE == XMODE_UP) ? a.sorted_pair[r] / a.kk : r;
+    it.xoff[tt] = static_cast<uint32_t>(tok) * row_bytes + 16 * lq;
   }
 }
 
-template <typename T, int MODE, int NT>
+template <typename T, int MODE, int NT, int SUB>
 __device__ __forceinline__ void witem_setup(const XArgs& a, const int* s_istart, const int* s_off,
-                                            int item, int lrow, int lq, size_t row_bytes,
+                                            int item, int lrow, int lq, uint32_t row_bytes,
                                             WItem<NT>& it) {
-  witem_weights<T, MODE, NT>(a, s_istart, s_off, item, lrow, lq, row_bytes, it);
-  witem_tokens<T, MODE, NT>(a, lrow, it);
+  witem_weights<T, MODE, NT, SUB>(a, s_istart, s_off, item, lrow, lq, row_bytes, it);
+  witem_tokens<T, MODE, NT>(a, lrow, lq, row_bytes, it);
 }
 
-// Weight bytes of chunk c in the load layout: register i holds row
-// 4*(i%4) + l/16, bytes 256*(i/4) + 16*(l%16) of the chunk.  Past the end of
-// K (partial last chunk) the lane re-reads the chunk's first bytes: finite
-// data that meets zero token fragments.  The loaded registers are never
-// touched until use, so the loads stay in flight.
-__device__ __forceinline__ void wload(const char* const (&wp)[4], int c, int kfrag_total, int lrow,
-                                      uint4 (&w)[CHUNK_FRAGS]) {
-  const int valid = (kfrag_total - c * CHUNK_FRAGS) * FRAG_BYTES;  // valid bytes in this chunk
-  const size_t cb = static_cast<size_t>(c) * CHUNK_BYTES;
+// Base of tile s (aliased to tile 0 past the matrix) of an item, at chunk c.
+template <int NT>
+__device__ __forceinline__ const char* tile_chunk(const WItem<NT>& it, int s, int c) {
+  return it.wbase + (s < it.n_sub ? s : 0) * it.sub_bytes + c * CHUNK_BYTES;
+}
+
+// Weight bytes of one tile-chunk in the load layout: register i holds row
+// 4*(i%4) + l/16, bytes 256*(i/4) + 16*(l%16) of the chunk.  Non-temporal:
+// streamed once.  The loaded registers are not touched until use, so the
+// loads stay in flight.
+__device__ __forceinline__ void wload_full(const char* cbase, const uint32_t (&woff)[4],
+                                           uint4 (&w)[CHUNK_FRAGS]) {
+#pragma unroll
+  for (int i = 0; i < CHUNK_FRAGS; ++i) w[i] = ldg_nt(cbase + 256 * (i / 4), woff[i % 4]);
+}
+// The last chunk of K when it is partial (valid < 512 bytes): lanes past
+// the end re-read the chunk's first bytes of their row (finite data that
+// meets zero token fragments).
+__device__ __forceinline__ void wload_part(const char* cbase, const uint32_t (&woff)[4], int valid,
+                                           int lrow, uint4 (&w)[CHUNK_FRAGS]) {
 #pragma unroll
   for (int i = 0; i < CHUNK_FRAGS; ++i) {
     const int col = 256 * (i / 4) + 16 * lrow;
-    const int colc = col < valid ? col : 0;
-    w[i] = ld16_nt(wp[i % 4] + cb + (colc - 16 * lrow));
+    w[i] = ldg_nt(cbase, woff[i % 4] + (col < valid ? 256 * (i / 4) : -16 * lrow));
   }
 }
+__device__ __forceinline__ void wload(const char* cbase, const uint32_t (&woff)[4], int valid, int lrow,
+                                      uint4 (&w)[CHUNK_FRAGS]) {
+  if (valid >= CHUNK_BYTES)
+    wload_full(cbase, woff, w);
+  else
+    wload_part(cbase, woff, valid, lrow, w);
+}
 
-// Token fragments of chunk c for every tile (past the end of K the lane
-// re-reads a valid fragment; wmma() zeroes those at use).
+// Token fragments of one chunk for every tile (cx = activations + chunk offset).
 template <int NT>
-__device__ __forceinline__ void xload(const char* act, const int (&tok)[NT], size_t row_bytes,
-                                      int lq, int c, int kfrag_total,
-                                      uint4 (&x)[NT][CHUNK_FRAGS]) {
-  const int nf = min(CHUNK_FRAGS, kfrag_total - c * CHUNK_FRAGS);
+__device__ __forceinline__ void xload_full(const char* cx, const uint32_t (&xoff)[NT],
+                                           uint4 (&x)[NT][CHUNK_FRAGS]) {
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    const char* p = act + static_cast<size_t>(tok[tt]) * row_bytes + lq * 16 +
-                    static_cast<size_t>(c) * CHUNK_BYTES;
+  for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-    for (int f = 0; f < CHUNK_FRAGS; ++f) {
-      x[tt][f] = ld16(p + min(f, nf - 1) * FRAG_BYTES);
-    }
-  }
+    for (int f = 0; f < CHUNK_FRAGS; ++f) x[tt][f] = ldg(cx + FRAG_BYTES * f, xoff[tt]);
+}
+// Partial chunk: fragments past the end of K re-read a valid one; wmma_part
+// zeroes them at use.
+template <int NT>
+__device__ __forceinline__ void xload_part(const char* cx, const uint32_t (&xoff)[NT], int nf,
+                                           uint4 (&x)[NT][CHUNK_FRAGS]) {
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+    for (int f = 0; f < CHUNK_FRAGS; ++f) x[tt][f] = ldg(cx, xoff[tt] + FRAG_BYTES * min(f, nf - 1));
 }
 
 constexpr int WT_ROW = CHUNK_BYTES + 16;  // padded row of the wave's LDS tile
@@ -228,49 +277,64 @@ __device__ __forceinline__ void wtranspose(const uint4 (&w)[CHUNK_FRAGS], char* 
     wt[f] = *reinterpret_cast<const uint4*>(tile + lrow * WT_ROW + FRAG_BYTES * f + 16 * lq);
 }
 
-// Fragments f >= nf lie past the end of K: their token side is zeroed here,
-// so they add exactly nothing whatever the weight side holds.  A tile past
-// the pass's rows (repeated rows) is multiplied too -- branching around it
-// costs more than the MFMAs -- and never stored.
+// A token tile past the pass's rows (repeated rows) is multiplied too --
+// branching around it costs more than the MFMAs -- and never stored.
 template <typename T, int NT>
-__device__ __forceinline__ void wmma(const uint4 (&w)[CHUNK_FRAGS], const uint4 (&x)[NT][CHUNK_FRAGS],
-                                     int nf, f32x4_t (&acc)[NT]) {
+__device__ __forceinline__ void wmma_full(const uint4 (&w)[CHUNK_FRAGS], const uint4 (&x)[NT][CHUNK_FRAGS],
+                                          f32x4_t (&acc)[NT]) {
+#pragma unroll
+  for (int f = 0; f < CHUNK_FRAGS; ++f)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = Elem<T>::mma(w[f], x[tt][f], acc[tt]);
+}
+// Fragments f >= nf lie past the end of K: their token side is zeroed here,
+// so they add exactly nothing whatever the weight side holds.
+template <typename T, int NT>
+__device__ __forceinline__ void wmma_part(const uint4 (&w)[CHUNK_FRAGS], const uint4 (&x)[NT][CHUNK_FRAGS],
+                                          int nf, f32x4_t (&acc)[NT]) {
 #pragma unroll
   for (int f = 0; f < CHUNK_FRAGS; ++f)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[tt] = Elem<T>::mma(w[f], keep_or_zero(f < nf, x[tt][f]), acc[tt]);
 }
 
-// acc[tt][r] = D[4*lq + r][lrow]: weight row 4*lq+r of the item's 16, token row tt*16+lrow.
-template <typename T, int MODE, int NT>
-__device__ __forceinline__ void wstore(const XArgs& a, const WItem<NT>& it, f32x4_t (&acc)[NT],
+// acc[s][tt][r] = D[4*lq + r][lrow] of tile s: weight row 4*lq+r of the
+// tile's 16, token row tt*16+lrow.  Tiles past the matrix are not stored.
+template <typename T, int MODE, int NT, int SUB>
+__device__ __forceinline__ void wstore(const XArgs& a, const WItem<NT>& it, f32x4_t (&acc)[SUB][NT],
                                        int lrow, int lq) {
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    const int tr = it.t0 + tt * 16 + lrow;
-    if (MODE == XMODE_UP) {
-      float up[4];
+  for (int s = 0; s < SUB; ++s) {
+    if (s < it.n_sub) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) up[r] = __shfl_xor(acc[tt][r], 32, WAVE);
-      const int n = it.n0 + 4 * lq;
-      if (lq < 2 && tr < it.m_end && n < a.I_loc) {
-        float o[4];
+      for (int tt = 0; tt < NT; ++tt) {
+        const int tr = it.t0 + tt * 16 + lrow;
+        if (MODE == XMODE_UP) {
+          float up[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float gt = acc[tt][r];
-          o[r] = gt / (1.0f + __expf(-gt)) * up[r];
+          for (int r = 0; r < 4; ++r) up[r] = __shfl_xor(acc[s][tt][r], 32, WAVE);
+          const int n = it.n0 + 8 * s + 4 * lq;
+          if (lq < 2 && tr < it.m_end) {
+            float o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float gt = acc[s][tt][r];
+              o[r] = gt / (1.0f + __expf(-gt)) * up[r];
+            }
+            T* dst = reinterpret_cast<T*>(a.out) + static_cast<size_t>(it.row0 + tr) * a.I_loc + n;
+            Elem<T>::store4(dst, o[0], o[1], o[2], o[3]);
+          }
+        } else {
+          const int n = it.n0 + 16 * s + 4 * lq;
+          if (tr < it.m_end) {
+            T* dst = reinterpret_cast<T*>(a.out) + static_cast<size_t>(it.row0 + tr) * a.H + n;
+            Elem<T>::store4(dst, acc[s][tt][0], acc[s][tt][1], acc[s][tt][2], acc[s][tt][3]);
+          }
         }
-        T* dst = reinterpret_cast<T*>(a.out) + static_cast<size_t>(it.row0 + tr) * a.I_loc + n;
-        Elem<T>::store4(dst, o[0], o[1], o[2], o[3]);
-      }
-    } else {
-      const int n = it.n0 + 4 * lq;
-      if (tr < it.m_end && n < a.H) {
-        T* dst = reinterpret_cast<T*>(a.out) + static_cast<size_t>(it.row0 + tr) * a.H + n;
-        Elem<T>::store4(dst, acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
       }
     }
-    acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -281,75 +345,81 @@ __device__ __forceinline__ int chunk_owner(long long q, long long Q, int W) {
 
 // A wave's partial of an item goes to slot 0 if the item is the first one its
 // range touches, else to slot 1 (a range has at most two split items).
-__device__ __forceinline__ float* part_slot(const XArgs& a, int NT, int w, int item, long long Q, int W) {
+__device__ __forceinline__ float* part_slot(const XArgs& a, int tiles, int w, int item, long long Q, int W) {
   const long long q0 = Q * w / W;
   const int which = (q0 / a.nck == item) ? 0 : 1;
-  return a.part + (static_cast<size_t>(w) * 2 + which) * NT * WAVE * 4;
+  return a.part + (static_cast<size_t>(w) * 2 + which) * tiles * WAVE * 4;
 }
 
 // The item's chunks were split over waves wa..wb (K order).  Store this
 // wave's partial; the last wave to arrive sums all of them in K order and
 // runs the epilogue.
-template <typename T, int MODE, int NT>
-__device__ __forceinline__ void finish_split(const XArgs& a, const WItem<NT>& it, f32x4_t (&acc)[NT],
+template <typename T, int MODE, int NT, int SUB>
+__device__ __forceinline__ void finish_split(const XArgs& a, const WItem<NT>& it, f32x4_t (&acc)[SUB][NT],
                                              int item, int w, int W, long long Q, int lrow, int lq) {
   const int l = lane_id();
   const long long qa = static_cast<long long>(item) * a.nck;
   const int wa = chunk_owner(qa, Q, W);
   const int wb = chunk_owner(qa + a.nck - 1, Q, W);
-  uint64_t* mine = reinterpret_cast<uint64_t*>(part_slot(a, NT, w, item, Q, W));
+  uint64_t* mine = reinterpret_cast<uint64_t*>(part_slot(a, SUB * NT, w, item, Q, W));
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    st_agent(mine + (tt * WAVE + l) * 2, (static_cast<uint64_t>(__float_as_uint(acc[tt][1])) << 32) |
-                                             __float_as_uint(acc[tt][0]));
-    st_agent(mine + (tt * WAVE + l) * 2 + 1, (static_cast<uint64_t>(__float_as_uint(acc[tt][3])) << 32) |
-                                                 __float_as_uint(acc[tt][2]));
-  }
+  for (int s = 0; s < SUB; ++s)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      uint64_t* p = mine + ((s * NT + tt) * WAVE + l) * 2;
+      st_agent(p, (static_cast<uint64_t>(__float_as_uint(acc[s][tt][1])) << 32) | __float_as_uint(acc[s][tt][0]));
+      st_agent(p + 1, (static_cast<uint64_t>(__float_as_uint(acc[s][tt][3])) << 32) | __float_as_uint(acc[s][tt][2]));
+    }
   __builtin_amdgcn_s_waitcnt(0);  // the partial is performed (agent scope) before the count
   int old = 0;
   if (l == 0) old = atomicAdd(a.ctr + item, 1);
   old = __shfl(old, 0, WAVE);
   if (old == wb - wa) {  // last to arrive (wave-uniform)
     if (l == 0) st_agent(a.ctr + item, 0);
-    f32x4_t sum[NT];
+    f32x4_t sum[SUB][NT];
     for (int v = wa; v <= wb; ++v) {
-      f32x4_t pv[NT];
       if (v == w) {
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) pv[tt] = acc[tt];
+        for (int s = 0; s < SUB; ++s)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) sum[s][tt] = (v == wa) ? acc[s][tt] : sum[s][tt] + acc[s][tt];
       } else {
-        const uint64_t* src = reinterpret_cast<const uint64_t*>(part_slot(a, NT, v, item, Q, W));
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(part_slot(a, SUB * NT, v, item, Q, W));
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          const uint64_t lo = ld_agent(src + (tt * WAVE + l) * 2);
-          const uint64_t hi = ld_agent(src + (tt * WAVE + l) * 2 + 1);
-          pv[tt] = f32x4_t{__uint_as_float(static_cast<uint32_t>(lo)), __uint_as_float(static_cast<uint32_t>(lo >> 32)),
-                           __uint_as_float(static_cast<uint32_t>(hi)), __uint_as_float(static_cast<uint32_t>(hi >> 32))};
-        }
+        for (int s = 0; s < SUB; ++s)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            const uint64_t* p = src + ((s * NT + tt) * WAVE + l) * 2;
+            const uint64_t lo = ld_agent(p);
+            const uint64_t hi = ld_agent(p + 1);
+            const f32x4_t pv = {__uint_as_float(static_cast<uint32_t>(lo)), __uint_as_float(static_cast<uint32_t>(lo >> 32)),
+                                __uint_as_float(static_cast<uint32_t>(hi)), __uint_as_float(static_cast<uint32_t>(hi >> 32))};
+            sum[s][tt] = (v == wa) ? pv : sum[s][tt] + pv;
+          }
       }
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) sum[tt] = (v == wa) ? pv[tt] : sum[tt] + pv[tt];
     }
-    wstore<T, MODE, NT>(a, it, sum, lrow, lq);
+    wstore<T, MODE, NT, SUB>(a, it, sum, lrow, lq);
   }
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < SUB; ++s)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-template <typename T, int MODE, int NT>
+template <typename T, int MODE, int NT, int SUB>
 __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   __shared__ int s_istart[MAX_GROUPS + 1];
   __shared__ int s_off[MAX_GROUPS + 1];
   __shared__ __attribute__((aligned(16))) char s_wt[XW_WAVES][16 * WT_ROW];
 
-  const int wv = threadIdx.x / WAVE;
+  const int wv = uni(threadIdx.x / WAVE);
   const int l = lane_id();
   const int lrow = l & 15;
   const int lq = l >> 4;
 
-  item_prefix<NT>(a.offsets, a.n_groups, a.n_tiles, s_istart, s_off);
+  item_prefix<NT>(a.offsets, a.n_groups, a.n_quads, s_istart, s_off);
   __syncthreads();  // the only barrier; waves are independent from here on
-  const long long Q = static_cast<long long>(s_istart[a.n_groups]) * a.nck;
+  const long long Q = static_cast<long long>(uni(s_istart[a.n_groups])) * a.nck;
   const int W = static_cast<int>(min(static_cast<long long>(a.waves), (Q + MIN_CPW - 1) / MIN_CPW));
   const int w = wv * gridDim.x + blockIdx.x;
   if (w >= W) return;  // wave-uniform
@@ -357,57 +427,82 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   const long long q1 = Q * (w + 1) / W;
   if (q0 >= q1) return;
 
-  const size_t row_bytes = static_cast<size_t>(a.K) * sizeof(T);
+  const uint32_t row_bytes = static_cast<uint32_t>(a.K) * sizeof(T);
   const char* act = reinterpret_cast<const char*>(a.act);
+  const int kbytes = a.kfrag_total * FRAG_BYTES;
 
   int item = static_cast<int>(q0 / a.nck);
   int cb = static_cast<int>(q0 - static_cast<long long>(item) * a.nck);   // first chunk of the item here
   int ce = static_cast<int>(min(static_cast<long long>(a.nck), q1 - static_cast<long long>(item) * a.nck));
+
   // The first weight chunk goes out before the token indices are fetched.
   WItem<NT> cur, nxt;
-  witem_weights<T, MODE, NT>(a, s_istart, s_off, item, lrow, lq, row_bytes, cur);
+  witem_weights<T, MODE, NT, SUB>(a, s_istart, s_off, item, lrow, lq, row_bytes, cur);
   uint4 w0[CHUNK_FRAGS], w1[CHUNK_FRAGS], x[NT][CHUNK_FRAGS];
   int c = cb;
-  wload(cur.wp, c, a.kfrag_total, lrow, w0);
-  witem_tokens<T, MODE, NT>(a, lrow, cur);
+  wload(tile_chunk(cur, 0, c), cur.woff, kbytes - c * CHUNK_BYTES, lrow, w0);
+  witem_tokens<T, MODE, NT>(a, lrow, lq, row_bytes, cur);
   bool have_nxt = static_cast<long long>(item + 1) * a.nck < q1;
-  if (have_nxt) witem_setup<T, MODE, NT>(a, s_istart, s_off, item + 1, lrow, lq, row_bytes, nxt);
+  if (have_nxt) witem_setup<T, MODE, NT, SUB>(a, s_istart, s_off, item + 1, lrow, lq, row_bytes, nxt);
 
-  f32x4_t acc[NT];
+  f32x4_t acc[SUB][NT];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < SUB; ++s)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   char* tile = s_wt[wv];
 
-  // One step: token fragments of (cur, c); weights of the next chunk into WN;
-  // multiply WC; at the end of the item's chunks in this range, finish it and
-  // move on (break when the range is done).
-#define XSTEP(WC, WN)                                                                     \
-  {                                                                                       \
-    xload<NT>(act, cur.tok, row_bytes, lq, c, a.kfrag_total, x);                          \
-    __builtin_amdgcn_sched_barrier(0); /* token loads stay ahead of the weight loads */   \
-    const bool last = c + 1 >= ce;                                                        \
-    /* One weight load on every path (next chunk, next item's first chunk, or with no  */ \
-    /* work left a harmless re-read of this chunk), so the same number of loads is     */ \
-    /* outstanding whichever way the step went and no wait drains the prefetch.        */ \
-    {                                                                                     \
-      const bool to_next = last && have_nxt;                                              \
-      const char* np[4];                                                                  \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) np[j] = to_next ? nxt.wp[j] : cur.wp[j]; \
-      wload(np, last ? (have_nxt ? 0 : c) : c + 1, a.kfrag_total, lrow, WN);              \
+  // Sub-step S of a chunk step: load the next tile-chunk into WN (tile S+1
+  // of this chunk; after the last tile, tile 0 of the next chunk, of the next
+  // item, or with no work left a harmless re-read), then multiply WC, the
+  // chunk of tile S, with the chunk's token fragments.  Full chunks take the
+  // plain paths; only a partial last chunk of K takes the masked ones, which
+  // issue the same loads, so the outstanding-load count never depends on the
+  // path.
+#define XSUB(S, WC, WN)                                                                   \
+  if constexpr (S < SUB) {                                                                \
+    if (S + 1 < SUB) {                                                                    \
+      wload(tile_chunk(cur, S + 1, c), cur.woff, cvalid, lrow, WN);                       \
+    } else if (!last) {                                                                   \
+      wload(tile_chunk(cur, 0, c + 1), cur.woff, cvalid - CHUNK_BYTES, lrow, WN);         \
+    } else if (have_nxt) {                                                                \
+      wload(tile_chunk(nxt, 0, 0), nxt.woff, kbytes, lrow, WN);                           \
+    } else {                                                                              \
+      wload(tile_chunk(cur, 0, c), cur.woff, cvalid, lrow, WN);                           \
     }                                                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                    \
-    {                                                                                     \
-      uint4 wt[CHUNK_FRAGS];                                                              \
-      wtranspose(WC, tile, lrow, lq, wt);                                                 \
-      wmma<T, NT>(wt, x, min(CHUNK_FRAGS, a.kfrag_total - c * CHUNK_FRAGS), acc);           \
-    }                                                                                     \
+    uint4 wt[CHUNK_FRAGS];                                                                \
+    wtranspose(WC, tile, lrow, lq, wt);                                                   \
+    if (cvalid >= CHUNK_BYTES)                                                            \
+      wmma_full<T, NT>(wt, x, acc[S]);                                                    \
+    else                                                                                  \
+      wmma_part<T, NT>(wt, x, cvalid / FRAG_BYTES, acc[S]);                               \
+  }
+
+  // One chunk step: the chunk's token fragments, then the SUB tiles (the
+  // register buffers alternate, starting with WA); at the end of the item's
+  // chunks in this range, finish it and move on (break when the range is
+  // done).
+#define CSTEP(WA, WB)                                                                     \
+  {                                                                                       \
+    const int cvalid = kbytes - c * CHUNK_BYTES; /* bytes of K left from this chunk on */ \
+    if (cvalid >= CHUNK_BYTES)                                                            \
+      xload_full<NT>(act + c * CHUNK_BYTES, cur.xoff, x);                                 \
+    else                                                                                  \
+      xload_part<NT>(act + c * CHUNK_BYTES, cur.xoff, cvalid / FRAG_BYTES, x);            \
+    __builtin_amdgcn_sched_barrier(0); /* token loads stay ahead of the weight loads */   \
+    const bool last = c + 1 >= ce;                                                        \
+    XSUB(0, WA, WB)                                                                       \
+    XSUB(1, WB, WA)                                                                       \
+    XSUB(2, WA, WB)                                                                       \
+    XSUB(3, WB, WA)                                                                       \
     if (!last) {                                                                          \
       ++c;                                                                                \
     } else {                                                                              \
       if (cb == 0 && ce == a.nck)                                                         \
-        wstore<T, MODE, NT>(a, cur, acc, lrow, lq);                                       \
+        wstore<T, MODE, NT, SUB>(a, cur, acc, lrow, lq);                                  \
       else                                                                                \
-        finish_split<T, MODE, NT>(a, cur, acc, item, w, W, Q, lrow, lq);                  \
+        finish_split<T, MODE, NT, SUB>(a, cur, acc, item, w, W, Q, lrow, lq);             \
       if (!have_nxt) break;                                                               \
       ++item;                                                                             \
       cur = nxt;                                                                          \
@@ -416,15 +511,21 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
       ce = static_cast<int>(min(static_cast<long long>(a.nck), q1 - static_cast<long long>(item) * a.nck)); \
       have_nxt = static_cast<long long>(item + 1) * a.nck < q1;                           \
       if (have_nxt)                                                                       \
-        witem_setup<T, MODE, NT>(a, s_istart, s_off, item + 1, lrow, lq, row_bytes, nxt);  \
+        witem_setup<T, MODE, NT, SUB>(a, s_istart, s_off, item + 1, lrow, lq, row_bytes, nxt); \
     }                                                                                     \
   }
 
-  while (true) {
-    XSTEP(w0, w1)
-    XSTEP(w1, w0)
+  static_assert(SUB == 1 || SUB == 2 || SUB == 4, "tiles per item");
+  if constexpr (SUB % 2 == 0) {
+    while (true) CSTEP(w0, w1)
+  } else {
+    while (true) {
+      CSTEP(w0, w1)
+      CSTEP(w1, w0)
+    }
   }
-#undef XSTEP
+#undef CSTEP
+#undef XSUB
 }
 
 // ---------------------------------------------------------------- host side
@@ -446,18 +547,27 @@ struct XShape {
 static XShape x_shape(int mode, int H, int I, int dtype) {
   XShape s{};
   const int K = mode == XMODE_UP ? H : I;
-  s.n_tiles = mode == XMODE_UP ? (I + 7) / 8 : (H + 15) / 16;
+  s.n_tiles = mode == XMODE_UP ? I / 8 : H / 16;
   s.kfrag_total = K * elem_bytes_x(dtype) / FRAG_BYTES;
   s.nck = (s.kfrag_total + CHUNK_FRAGS - 1) / CHUNK_FRAGS;
   return s;
 }
 
+// Weight tiles per item: four when the token side is reused enough to matter
+// (two token tiles) or when a tile alone is too small to be a work item
+// (under 16 KB); else one.
+static int pick_sub(int nt, int kfrag_total) {
+  const long long tile_bytes = 16LL * kfrag_total * FRAG_BYTES;
+  return (nt == 2 || tile_bytes < 16384) ? 4 : 1;
+}
+
 // Items of one launch at most: sum over groups of ceil(m_g / 16) passes
-// <= pairs / 16 + touched groups (NT = 1 is the largest count).
-static long long max_items(const XShape& s, int T, int kk, int n_groups) {
+// <= pairs / 16 + touched groups (NT = 1 is the largest count), each of
+// n_tiles / sub items.
+static long long max_items(const XShape& s, int sub, int T, int kk, int n_groups) {
   const long long pairs = static_cast<long long>(T) * kk;
   const long long touched = n_groups < pairs ? n_groups : pairs;
-  return (pairs / 16 + touched) * s.n_tiles;
+  return (pairs / 16 + touched) * ((s.n_tiles + sub - 1) / sub);
 }
 
 static size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
@@ -474,20 +584,26 @@ static XWorkspace x_workspace(int T, int kk, int n_groups, int H, int I, int dty
   long long items = 0, waves = 0;
   for (int mode = XMODE_UP; mode <= XMODE_DOWN; ++mode) {
     const XShape s = x_shape(mode, H, I, dtype);
-    const long long it = max_items(s, T, kk, n_groups);
+    const long long it = max_items(s, 1, T, kk, n_groups);  // the most items any choice of tiles gives
     long long wv = (it * s.nck + MIN_CPW - 1) / MIN_CPW;
     if (wv > MAX_WAVES) wv = MAX_WAVES;
     if (it > items) items = it;
     if (wv > waves) waves = wv;
   }
   w.ctr_bytes = round256(static_cast<size_t>(items) * sizeof(int));
-  w.part_bytes = static_cast<size_t>(waves) * 2 * NT_MAX * WAVE * 4 * sizeof(float);
+  w.part_bytes = static_cast<size_t>(waves) * 2 * SUB_MAX * NT_MAX * WAVE * 4 * sizeof(float);
   return w;
 }
 
 bool expert_items_fit(int T, int kk, int n_groups, int H, int I, int dtype) {
   for (int mode = XMODE_UP; mode <= XMODE_DOWN; ++mode)
-    if (max_items(x_shape(mode, H, I, dtype), T, kk, n_groups) > 0x7fffffffLL) return false;
+    if (max_items(x_shape(mode, H, I, dtype), 1, T, kk, n_groups) > 0x7fffffffLL) return false;
+  // Lane offsets are 32-bit: a group's W13 slice, the activations and `a`
+  // must each stay below 2 GiB.
+  const long long e = elem_bytes_x(dtype);
+  if (2LL * I * H * e >= (1LL << 31)) return false;
+  if (static_cast<long long>(T) * H * e >= (1LL << 31)) return false;
+  if (static_cast<long long>(T) * kk * I * e >= (1LL << 31)) return false;
   return true;
 }
 
@@ -497,13 +613,13 @@ size_t expert_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dty
   return w.ctr_bytes + w.part_bytes;
 }
 
-template <typename T, int MODE, int NT>
+template <typename T, int MODE, int NT, int SUB>
 static int resident_blocks() {
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&expert_wave_kernel<T, MODE, NT>), XW_WAVES * WAVE, 0) !=
+            &n, reinterpret_cast<const void*>(&expert_wave_kernel<T, MODE, NT, SUB>), XW_WAVES * WAVE, 0) !=
             hipSuccess || n < 1)
       n = 1;
     per_cu = n;
@@ -513,11 +629,19 @@ static int resident_blocks() {
   return static_cast<int>(g);
 }
 
-template <typename T, int MODE, int NT>
+template <typename T, int MODE, int NT, int SUB>
 static void launch_t(XArgs a, hipStream_t s) {
-  const int grid = resident_blocks<T, MODE, NT>();
+  const int grid = resident_blocks<T, MODE, NT, SUB>();
   a.waves = grid * XW_WAVES;
-  hipLaunchKernelGGL((expert_wave_kernel<T, MODE, NT>), dim3(grid), dim3(XW_WAVES * WAVE), 0, s, a);
+  a.n_quads = (a.n_tiles + SUB - 1) / SUB;
+  hipLaunchKernelGGL((expert_wave_kernel<T, MODE, NT, SUB>), dim3(grid), dim3(XW_WAVES * WAVE), 0, s, a);
+}
+
+template <typename T, int MODE>
+static void launch_tm(XArgs a, int nt, int sub, hipStream_t s) {
+  if (nt == 2) launch_t<T, MODE, 2, 4>(a, s);
+  else if (sub == 4) launch_t<T, MODE, 1, 4>(a, s);
+  else launch_t<T, MODE, 1, 1>(a, s);
 }
 
 template <int MODE>
@@ -529,14 +653,12 @@ static void launch_mode(int dtype, XArgs a, int T, int kk, void* ws, hipStream_t
   a.ctr = static_cast<int*>(ws);
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                     x_workspace(T, kk, a.n_groups, a.H, a.I_loc, dtype).ctr_bytes);
-  const bool nt2 = pick_nt(T, kk, a.n_groups) == 2;
-  if (dtype == 1) {
-    if (nt2) launch_t<uint16_t, MODE, 2>(a, s);
-    else launch_t<uint16_t, MODE, 1>(a, s);
-  } else {
-    if (nt2) launch_t<float, MODE, 2>(a, s);
-    else launch_t<float, MODE, 1>(a, s);
-  }
+  const int nt = pick_nt(T, kk, a.n_groups);
+  const int sub = pick_sub(nt, sh.kfrag_total);
+  if (dtype == 1)
+    launch_tm<uint16_t, MODE>(a, nt, sub, s);
+  else
+    launch_tm<float, MODE>(a, nt, sub, s);
 }
 
 void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, const int32_t* offsets,
