@@ -8,25 +8,26 @@
 //   dst13[q] (E_local, 2I/P, H): rows S_q of the gate half, then rows S_q of
 //                                the up half, of every local expert
 //   dst2[q]  (E_local, H, I/P):  columns S_q of every W2 row
-// One launch walks both source tensors in address order, 16 bytes per lane:
-// reads are fully coalesced, each W13 row lands as one contiguous row and
-// each W2 row splits into P contiguous segments.  Every byte is read once and
-// written once; the copy is exact.
+// One launch walks both source tensors row by row (a wave per row, 16 bytes
+// per lane): reads are fully coalesced, each W13 row lands as one contiguous
+// row and each W2 row splits into P contiguous segments.  Every byte is read
+// once and written once; the copy is exact.
 #include "common.hpp"
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int REPACK_THREADS = 256;
-constexpr int REPACK_UNROLL = 4;
+constexpr int RP_WAVES = 4;                 // waves per block
+constexpr int RP_U = 8;                     // 16-byte chunks per lane per step
+constexpr int RP_STEP = RP_U * WAVE;        // chunks per wave per step
 
 struct RepackArgs {
   const char* w13;
   const char* w2;
   PeerPtrs d13;
   PeerPtrs d2;
-  long long chunks13;  // 16-byte chunks in W13
-  long long chunks2;   // 16-byte chunks in W2
+  long long rows13;    // E_local * 2I source rows of W13
+  long long rows2;     // E_local * H source rows of W2
   int row13;           // chunks per W13 row (H * elem / 16)
   int row2;            // chunks per W2 row (I * elem / 16)
   int I;               // rows per half of W13
@@ -34,44 +35,66 @@ struct RepackArgs {
   int seg2;            // chunks per W2 segment (Ip * elem / 16)
 };
 
-__device__ __forceinline__ char* repack_dst(const RepackArgs& a, long long c) {
-  if (c < a.chunks13) {
-    const long long row = c / a.row13;
-    const int col = static_cast<int>(c - row * a.row13);
-    const long long e = row / (2 * a.I);
-    const int i2 = static_cast<int>(row - e * 2 * a.I);
-    const int half = i2 / a.I;
+// One wave copies whole source rows, in address order, RP_U chunks per lane
+// per step with all loads issued before the stores.  A W13 row has one
+// wave-uniform destination row; a W2 row falls into P segments, and which
+// segment (and where in it) a lane's chunk of a step lands is the same for
+// every W2 row, so it is worked out once per lane.
+__global__ __launch_bounds__(RP_WAVES * WAVE) void repack_kernel(RepackArgs a) {
+  const int l = lane_id();
+  const long long nw = static_cast<long long>(gridDim.x) * RP_WAVES;
+  const long long w0 = static_cast<long long>(blockIdx.x) * RP_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+
+  // ---- W13: row (e, half, i) -> block q = i / Ip, row e*2Ip + half*Ip + i%Ip
+  for (long long r = w0; r < a.rows13; r += nw) {
+    const long long e = r / (2 * a.I);
+    const int i2 = static_cast<int>(r - e * 2 * a.I);
+    const int half = i2 >= a.I;
     const int i = i2 - half * a.I;
     const int q = i / a.Ip;
     const long long drow = e * 2 * a.Ip + half * a.Ip + (i - q * a.Ip);
-    return static_cast<char*>(a.d13.p[q]) + (drow * a.row13 + col) * 16;
-  }
-  c -= a.chunks13;
-  const long long row = c / a.row2;  // (e, h) row of W2
-  const int col = static_cast<int>(c - row * a.row2);
-  const int q = col / a.seg2;
-  return static_cast<char*>(a.d2.p[q]) + (row * a.seg2 + (col - q * a.seg2)) * 16;
-}
-
-__device__ __forceinline__ const char* repack_src(const RepackArgs& a, long long c) {
-  return c < a.chunks13 ? a.w13 + c * 16 : a.w2 + (c - a.chunks13) * 16;
-}
-
-__global__ __launch_bounds__(REPACK_THREADS) void repack_kernel(RepackArgs a) {
-  const long long total = a.chunks13 + a.chunks2;
-  const long long stride = static_cast<long long>(gridDim.x) * REPACK_THREADS;
-  long long c = static_cast<long long>(blockIdx.x) * REPACK_THREADS + threadIdx.x;
-  for (; c < total; c += stride * REPACK_UNROLL) {
-    u32x4_t v[REPACK_UNROLL];
+    const char* src = a.w13 + r * a.row13 * 16;
+    char* dst = static_cast<char*>(a.d13.p[q]) + drow * a.row13 * 16;
+    for (int c0 = 0; c0 < a.row13; c0 += RP_STEP) {
+      u32x4_t v[RP_U];
 #pragma unroll
-    for (int u = 0; u < REPACK_UNROLL; ++u) {
-      const long long cu = c + u * stride;
-      if (cu < total) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(repack_src(a, cu)));
+      for (int u = 0; u < RP_U; ++u) {
+        const int c = c0 + u * WAVE + l;
+        if (c < a.row13) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + c * 16));
+      }
+#pragma unroll
+      for (int u = 0; u < RP_U; ++u) {
+        const int c = c0 + u * WAVE + l;
+        if (c < a.row13) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4_t*>(dst + c * 16));
+      }
     }
+  }
+
+  // ---- W2: row r, chunk c -> block q = c / seg2, offset r*seg2 + c%seg2
+  for (int c0 = 0; c0 < a.row2; c0 += RP_STEP) {
+    char* dbase[RP_U];
+    int dcol[RP_U];
 #pragma unroll
-    for (int u = 0; u < REPACK_UNROLL; ++u) {
-      const long long cu = c + u * stride;
-      if (cu < total) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4_t*>(repack_dst(a, cu)));
+    for (int u = 0; u < RP_U; ++u) {
+      const int c = c0 + u * WAVE + l;
+      const int q = c < a.row2 ? c / a.seg2 : 0;
+      dbase[u] = static_cast<char*>(a.d2.p[q]);
+      dcol[u] = c - q * a.seg2;
+    }
+    for (long long r = w0; r < a.rows2; r += nw) {
+      const char* src = a.w2 + r * a.row2 * 16;
+      u32x4_t v[RP_U];
+#pragma unroll
+      for (int u = 0; u < RP_U; ++u) {
+        const int c = c0 + u * WAVE + l;
+        if (c < a.row2) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + c * 16));
+      }
+#pragma unroll
+      for (int u = 0; u < RP_U; ++u) {
+        const int c = c0 + u * WAVE + l;
+        if (c < a.row2)
+          __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4_t*>(dbase[u] + (r * a.seg2 + dcol[u]) * 16));
+      }
     }
   }
 }
@@ -86,16 +109,18 @@ void launch_repack_ep_to_tp(int dtype, const void* w13, const void* w2, int E_lo
   a.d2 = d2;
   a.row13 = H * eb / 16;
   a.row2 = I * eb / 16;
-  a.chunks13 = static_cast<long long>(E_local) * 2 * I * a.row13;
-  a.chunks2 = static_cast<long long>(E_local) * H * a.row2;
+  a.rows13 = static_cast<long long>(E_local) * 2 * I;
+  a.rows2 = static_cast<long long>(E_local) * H;
   a.I = I;
   a.Ip = I / P;
   a.seg2 = a.Ip * eb / 16;
-  const long long total = a.chunks13 + a.chunks2;
-  long long want = (total + REPACK_THREADS * REPACK_UNROLL - 1) / (REPACK_THREADS * REPACK_UNROLL);
-  const long long cap = static_cast<long long>(device_cu_count()) * 8;
-  const int grid = static_cast<int>(want < cap ? (want > 0 ? want : 1) : cap);
-  hipLaunchKernelGGL(repack_kernel, dim3(grid), dim3(REPACK_THREADS), 0, s, a);
+  // Enough waves to keep every CU streaming, never more than there are rows.
+  const long long rows = a.rows13 > a.rows2 ? a.rows13 : a.rows2;
+  long long grid = static_cast<long long>(device_cu_count()) * 8;
+  const long long need = (rows + RP_WAVES - 1) / RP_WAVES;
+  if (grid > need) grid = need;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(repack_kernel, dim3(static_cast<unsigned>(grid)), dim3(RP_WAVES * WAVE), 0, s, a);
 }
 
 }  // namespace moe
