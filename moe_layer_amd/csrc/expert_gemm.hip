@@ -7,7 +7,10 @@
 //
 // Decode-shaped problems are HBM-bound: every weight byte must stream from
 // HBM exactly once while the token side (a few to a few dozen rows per
-// expert) is small and stays in L2.
+// expert) is small and stays in L2.  At larger batches (bf16, T > 256) the
+// groups with more than 32 rows may have been taken by the LDS-tiled kernels
+// (expert_tile.hip) launched just before; this kernel re-derives that
+// decision from the same counts and skips exactly those groups.
 //
 // Work item = (group g, SUB adjacent weight tiles (1 or 4, per launch), pass
 // of 16 token rows -- 32 in the two-tile kernel when the group has more than
@@ -86,6 +89,8 @@ struct XArgs {
   int n_quads;             // items per pass: ceil(n_tiles / SUB) (SUB = weight tiles per item)
   int nck;                 // 512-byte chunks per item
   int waves;               // waves launched
+  int tile_nt;             // > 0: the tile kernel ran first with this many weight tiles per group ...
+  int tile_min;            // ... and took the groups above TILE_M_MIN rows if they made this many tiles
   int* ctr;                // per-item arrival counters (zero between calls)
   float* part;             // per-wave partial tiles: [wave][2][SUB][NT][64 lanes][4]
 };
@@ -101,9 +106,22 @@ __device__ __forceinline__ int pass_rows(int m) {
 // (passes x quads each); s_istart[n_groups] = total items.
 template <int NT>
 __device__ __forceinline__ void item_prefix(const int* __restrict__ offsets, int n_groups, int n_quads,
-                                            int* s_istart, int* s_off) {
+                                            int tile_nt, int tile_min, int* s_istart, int* s_off) {
   if (threadIdx.x >= WAVE) return;
   const int l = lane_id();
+  // The tile kernel's decision, by the same formula: it took the groups with
+  // more than TILE_M_MIN rows if they make at least tile_min tiles.
+  int m_max = 0x7fffffff;
+  if (tile_nt > 0) {
+    int tiles = 0;
+    for (int g = l; g < n_groups; g += WAVE) {
+      const int m = offsets[g + 1] - offsets[g];
+      if (m > TILE_M_MIN) tiles += (m + TILE_ROWS - 1) / TILE_ROWS * tile_nt;
+    }
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) tiles += __shfl_xor(tiles, d, WAVE);
+    if (tiles >= tile_min) m_max = TILE_M_MIN;
+  }
   int base = 0;
   for (int g0 = 0; g0 <= n_groups; g0 += WAVE) {
     const int g = g0 + l;
@@ -112,7 +130,7 @@ __device__ __forceinline__ void item_prefix(const int* __restrict__ offsets, int
     if (g < n_groups) {
       const int m = offsets[g + 1] - offsets[g];
       const int ps = pass_rows<NT>(m);
-      v = (m + ps - 1) / ps * n_quads;
+      if (m <= m_max) v = (m + ps - 1) / ps * n_quads;
     }
     const int incl = wave_inclusive_scan(v);
     if (g < n_groups) s_istart[g] = base + incl - v;
@@ -417,7 +435,7 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   const int lrow = l & 15;
   const int lq = l >> 4;
 
-  item_prefix<NT>(a.offsets, a.n_groups, a.n_quads, s_istart, s_off);
+  item_prefix<NT>(a.offsets, a.n_groups, a.n_quads, a.tile_nt, a.tile_min, s_istart, s_off);
   __syncthreads();  // the only barrier; waves are independent from here on
   const long long Q = static_cast<long long>(uni(s_istart[a.n_groups])) * a.nck;
   const int W = static_cast<int>(min(static_cast<long long>(a.waves), (Q + MIN_CPW - 1) / MIN_CPW));
@@ -607,10 +625,16 @@ bool expert_items_fit(int T, int kk, int n_groups, int H, int I, int dtype) {
   return true;
 }
 
+// Layout: the wave-streaming kernel's counters and partials, then (256-byte
+// aligned) the tile kernels' region.
+static size_t stream_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dtype) {
+  const XWorkspace w = x_workspace(T, kk, n_groups, H, I, dtype);
+  return round256(w.ctr_bytes + w.part_bytes);
+}
+
 size_t expert_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dtype) {
   if (T <= 0) return 0;
-  const XWorkspace w = x_workspace(T, kk, n_groups, H, I, dtype);
-  return w.ctr_bytes + w.part_bytes;
+  return stream_workspace_bytes(T, kk, n_groups, H, I, dtype) + expert_tile_workspace_bytes(T, kk, n_groups, H, I, dtype);
 }
 
 template <typename T, int MODE, int NT, int SUB>
@@ -646,6 +670,8 @@ static void launch_tm(XArgs a, int nt, int sub, hipStream_t s) {
 
 template <int MODE>
 static void launch_mode(int dtype, XArgs a, int T, int kk, void* ws, hipStream_t s) {
+  a.tile_nt = expert_tile_used(T, dtype) ? expert_tile_nt(MODE == XMODE_UP, a.H, a.I_loc) : 0;
+  a.tile_min = expert_tile_min_tiles();
   const XShape sh = x_shape(MODE, a.H, a.I_loc, dtype);
   a.n_tiles = sh.n_tiles;
   a.kfrag_total = sh.kfrag_total;
@@ -675,6 +701,9 @@ void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, cons
   a.K = H;
   a.I_loc = I;
   a.H = H;
+  if (expert_tile_used(T, dtype))
+    launch_expert_up_tiles(x, sorted_pair, offsets, n_groups, T, kk, w13, H, I, A,
+                           static_cast<char*>(ws) + stream_workspace_bytes(T, kk, n_groups, H, I, dtype), s);
   launch_mode<XMODE_UP>(dtype, a, T, kk, ws, s);
 }
 
@@ -690,6 +719,9 @@ void launch_expert_down(int dtype, const void* A, const int32_t* offsets, int n_
   a.K = I;
   a.I_loc = I;
   a.H = H;
+  if (expert_tile_used(T, dtype))
+    launch_expert_down_tiles(A, offsets, n_groups, T, kk, w2, H, I, y_pair,
+                             static_cast<char*>(ws) + stream_workspace_bytes(T, kk, n_groups, H, I, dtype), s);
   launch_mode<XMODE_DOWN>(dtype, a, T, kk, ws, s);
 }
 

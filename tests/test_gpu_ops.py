@@ -25,6 +25,50 @@ def test_ragged_batches(T, dtype):
     gh.check_layer(d, cfg, gh.gpu_layer(d, cfg))
 
 
+# For T > 256 (bf16), groups with more than 32 rows go to the LDS-tiled
+# kernels (128 token rows x 128 weight rows per tile, K split over blocks
+# stream-K style) when they make at least a third of a tile per compute
+# unit; otherwise the wave-streaming kernel keeps them.  These shapes put
+# ragged groups on both sides of the 32-row line, leave every kind of
+# partial tile (I' and H not multiples of 64 / 128, K ending half-way
+# through a 64-element stage: H = 1568, I' = 736), several token tiles per
+# group, shared groups, both views, and one case with too few tiles.
+@pytest.mark.parametrize("H,E,k,I,T,n_shared,view,P", [
+    (1568, 8, 2, 736, 300, 0, "full", 1),    # ragged, partial tiles and stages
+    (1536, 4, 2, 768, 600, 0, "full", 1),    # ~300 rows per group: 3 token tiles
+    (1536, 16, 4, 768, 300, 2, "full", 1),   # shared groups, some routed groups streamed
+    (2048, 16, 4, 1536, 300, 0, "tp", 2),    # TP slice: I' = 768
+    (1536, 16, 4, 768, 600, 0, "ep", 2),     # EP share of 8 experts
+    (1536, 4, 1, 768, 300, 0, "full", 1),    # too few tiles: all groups streamed
+])
+def test_tiled_groups(H, E, k, I, T, n_shared, view, P):
+    import gpu_helpers as gh
+    cfg = small(H=H, E=E, k=k, I=I, T=T, n_shared=n_shared, view=view, P=P, renorm=n_shared == 0)
+    d = make_layer_inputs(cfg, T, routing="uniform", rank=P - 1, seed=H + T + 1)  # no near-ties
+    print(f"[case] tiled H={H} E={E} k={k} I={I} T={T} shared={n_shared} {view} P={P}", flush=True)
+    g = gh.gpu_layer(d, cfg)
+    counts = g["counts"]
+    assert counts.max() > 32, counts  # groups on the tiled side of the line
+    gh.check_layer(d, cfg, g)
+
+
+# A single hot expert holding every token: one group far above the 32-row
+# line, too few tiles for the tiled kernels, so the wave-streaming kernel
+# takes it in passes of 32 rows.
+@pytest.mark.parametrize("T", [33, 64, 300])
+def test_hot_expert_split_tiles(T):
+    import gpu_helpers as gh
+    cfg = small(H=2048, E=8, k=2, I=1024, T=T)
+    d = make_layer_inputs(cfg, T, routing="uniform", seed=T)
+    b = np.zeros(8, dtype=np.float32)
+    b[5] = 40.0            # every token picks expert 5 first
+    d["gate_bias"] = b
+    print(f"[case] hot expert T={T}", flush=True)
+    g = gh.gpu_layer(d, cfg)
+    assert g["counts"][5] == T
+    gh.check_layer(d, cfg, g)
+
+
 @pytest.mark.parametrize("n_shared,renorm", [(2, False), (1, True)])
 def test_shared_experts(n_shared, renorm):
     import gpu_helpers as gh
