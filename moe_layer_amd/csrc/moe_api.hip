@@ -222,6 +222,7 @@ int moe_repack_ep_to_tp(const void* w13_ep, const void* w2_ep, int E_local, int 
   const int eb = elem_bytes(dtype);
   if ((static_cast<long long>(I / P) * eb) % 16 != 0 || (static_cast<long long>(H) * eb) % 16 != 0)
     return MOE_EUNSUPPORTED;
+  if (!repack_fits(E_local, H, I, dtype)) return MOE_EUNSUPPORTED;
   if (!w13_ep || !w2_ep || !dst13 || !dst2 || !aligned16(w13_ep) || !aligned16(w2_ep)) return MOE_EINVAL;
   PeerPtrs d13{}, d2{};
   for (int q = 0; q < P; ++q) {

@@ -69,7 +69,9 @@ void launch_combine(int dtype, const void* y_pair, const int32_t* pair_pos, cons
 struct PeerPtrs {
   void* p[MAX_P];
 };
-// EP -> TP local permute of expert weights into P per-peer blocks
+// EP -> TP local permute of expert weights into P per-peer blocks (whether
+// its 32-bit unit indexing covers these sizes)
+bool repack_fits(int E_local, int H, int I, int dtype);
 void launch_repack_ep_to_tp(int dtype, const void* w13, const void* w2, int E_local, int H, int I,
                             int P, const PeerPtrs& d13, const PeerPtrs& d2, hipStream_t s);
 

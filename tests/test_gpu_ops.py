@@ -162,9 +162,12 @@ def test_permute_empty_batch_writes_zero_counts():
     assert counts.cpu().tolist() == [0] * 9 and offsets.cpu().tolist() == [0] * 10
 
 
+# W2 rows of 1..4 chunks per lane (several rows per wave step, row counts
+# that do not divide evenly) and of more (one row at a time).
 @pytest.mark.parametrize("dtype,P,E_l,H,I", [
     ("bf16", 1, 2, 256, 64), ("bf16", 2, 3, 128, 64), ("bf16", 8, 2, 512, 128),
     ("fp32", 4, 3, 64, 32), ("bf16", 16, 1, 64, 128),
+    ("bf16", 8, 1, 64, 1536), ("bf16", 4, 2, 40, 1024), ("fp32", 2, 1, 56, 1024), ("bf16", 2, 2, 48, 2560),
 ])
 def test_repack_small(dtype, P, E_l, H, I):
     import torch
