@@ -8,10 +8,17 @@
 //   dst13[q] (E_local, 2I/P, H): rows S_q of the gate half, then rows S_q of
 //                                the up half, of every local expert
 //   dst2[q]  (E_local, H, I/P):  columns S_q of every W2 row
-// One launch walks both source tensors row by row (a wave per row, 16 bytes
-// per lane): reads are fully coalesced, each W13 row lands as one contiguous
-// row and each W2 row splits into P contiguous segments.  Every byte is read
-// once and written once; the copy is exact.
+// Two launches, each with exactly the blocks that fit on the chip at once:
+//   W13: each source row lands whole as one destination row; waves copy 4 KB
+//        units (16 bytes per lane, four per lane in flight, the next unit's
+//        loads issued before this unit's stores) in destination order, so the
+//        writes in flight fill one block front to back;
+//   W2:  each source row splits into P segments of I/P columns; a wave copies
+//        a few whole consecutive rows per step, with lanes assigned by
+//        destination so that every store instruction writes 1 KB of one or two
+//        blocks.
+// Every byte is read once and written once (non-temporal: streamed); the copy
+// is exact.
 #include "common.hpp"
 #include "moe_internal.h"
 
@@ -114,11 +121,7 @@ __device__ __forceinline__ void repack_w2_blocks(const RepackArgs& a, long long 
   }
 }
 
-// One wave copies whole source rows, in address order, RP_U chunks per lane
-// per step with all loads issued before the stores.  A W13 row has one
-// wave-uniform destination row; a W2 row falls into P segments, and which
-// segment (and where in it) a lane's chunk of a step lands is the same for
-// every W2 row, so it is worked out once per lane.
+// W13 part.  A unit's destination row is wave-uniform.
 __global__ __launch_bounds__(RP_WAVES * WAVE) void repack13_kernel(RepackArgs a) {
   const int l = lane_id();
   const long long nw = static_cast<long long>(gridDim.x) * RP_WAVES;
@@ -199,6 +202,8 @@ __global__ __launch_bounds__(RP_WAVES * WAVE) void repack2_kernel(RepackArgs a) 
     repack_w2_rows<PATH>(a, w0, nw, l);
   } else {
     for (int c0 = 0; c0 < a.row2; c0 += RP_STEP) {
+      // row by row: which segment (and where in it) a lane's chunk of a step
+      // lands is the same for every row, so it is worked out once per lane
       char* dbase[RP_U];
       int dcol[RP_U];
 #pragma unroll
