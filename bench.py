@@ -33,7 +33,8 @@ PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "expert_up_counters.json")
 
 def bench_repack(steps, warmup):
     """EP->TP local permute of one Qwen3-235B-shaped EP rank (16 experts, P=8):
-    a pure copy of 604 MB read + 604 MB written."""
+    a pure copy of 604 MB read + 604 MB written; the TP->EP inverse (the
+    switch back) is timed beside it."""
     import torch
 
     import moe_layer_amd
@@ -46,18 +47,25 @@ def bench_repack(steps, warmup):
     P, E_l, Ip = cfg.P, cfg.E // cfg.P, cfg.I // cfg.P
     d13 = [torch.empty((E_l, 2 * Ip, cfg.H), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
     d2 = [torch.empty((E_l, cfg.H, Ip), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
-    for _ in range(warmup):
-        moe_layer_amd.moe_repack_ep_to_tp(w13, w2, P, d13, d2)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        moe_layer_amd.moe_repack_ep_to_tp(w13, w2, P, d13, d2)
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / steps * 1e-3
+    r13, r2 = torch.empty_like(w13), torch.empty_like(w2)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e-3
+
+    t = timed(lambda: moe_layer_amd.moe_repack_ep_to_tp(w13, w2, P, d13, d2))
+    t_back = timed(lambda: moe_layer_amd.moe_repack_tp_to_ep(d13, d2, P, r13, r2))
     moved = 2 * (w13.numel() + w2.numel()) * 2
     gbs = moved / t / 1e9
+    gbs_back = moved / t_back / 1e9
     return {
         "metric": "EP->TP expert-weight repack throughput (read + write)",
         "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
@@ -67,6 +75,8 @@ def bench_repack(steps, warmup):
                    "bytes_read": moved // 2, "bytes_written": moved // 2},
         "roofline": {"bound": "hbm", "kernel": "repack", "achieved": gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "tp_to_ep": {"ms_per_step": t_back * 1e3, "achieved_GBs": gbs_back,
+                     "frac": gbs_back / HBM_PEAK_GBS},
     }
 
 

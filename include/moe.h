@@ -194,6 +194,23 @@ int moe_combine(const void* y_pair, const int32_t* pair_pos, const float* topk_w
 int moe_repack_ep_to_tp(const void* w13_ep, const void* w2_ep, int E_local, int H, int I, int P,
                         int dtype, void* const* dst13, void* const* dst2, hipStream_t stream);
 
+/*
+ * moe_repack_tp_to_ep -- local-permute phase of the TP->EP expert-weight
+ * reshard (Moebius review, §3.1 and Fig. 4, the switch back): after the
+ * exchange this rank holds, from each peer q < P, peer q's TP slice of this
+ * rank's E_local experts; rebuild the whole experts from those P blocks.  The
+ * exact inverse of moe_repack_ep_to_tp:
+ *   w13_ep[e] rows [q I/P, (q+1) I/P)     = src13[q][e] rows [0, I/P)
+ *   w13_ep[e] rows I + [q I/P, (q+1) I/P) = src13[q][e] rows [I/P, 2I/P)
+ *   w2_ep[e][:, q I/P .. (q+1) I/P)       = src2[q][e]
+ *   src13, src2: HOST arrays of P device pointers, (E_local, 2I/P, H) and
+ *   (E_local, H, I/P) dtype; w13_ep (E_local, 2I, H), w2_ep (E_local, H, I)
+ *   dtype [out], exact byte copies (outputs must not overlap the blocks).
+ * Limits: those of moe_repack_ep_to_tp.
+ */
+int moe_repack_tp_to_ep(const void* const* src13, const void* const* src2, int E_local, int H, int I, int P,
+                        int dtype, void* w13_ep, void* w2_ep, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

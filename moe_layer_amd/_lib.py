@@ -22,7 +22,7 @@ MOE_OP_EXPERT_UP, MOE_OP_EXPERT_DOWN = 5, 6
 EXPORTED = (
     "moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes",
     "moe_route", "moe_route_permute", "moe_permute", "moe_grouped_gemm", "moe_expert_up",
-    "moe_expert_down", "moe_combine", "moe_repack_ep_to_tp",
+    "moe_expert_down", "moe_combine", "moe_repack_ep_to_tp", "moe_repack_tp_to_ep",
 )
 
 
@@ -74,6 +74,9 @@ def lib():
     L.moe_repack_ep_to_tp.restype = _i
     L.moe_repack_ep_to_tp.argtypes = [_p, _p, _i, _i, _i, _i, _i, ctypes.POINTER(_p),
                                       ctypes.POINTER(_p), _p]
+    L.moe_repack_tp_to_ep.restype = _i
+    L.moe_repack_tp_to_ep.argtypes = [ctypes.POINTER(_p), ctypes.POINTER(_p), _i, _i, _i, _i, _i, _p, _p,
+                                      _p]
     _lib = L
     return L
 
@@ -242,3 +245,19 @@ def moe_repack_ep_to_tp(w13_ep, w2_ep, P, dst13, dst2, stream=None):
         _ptr(w13_ep, "w13_ep"), _ptr(w2_ep, "w2_ep", w13_ep.dtype, (E_l, H, I)), E_l, H, I, P,
         _dtype_code(w13_ep), arr13, arr2, _stream(stream))
     _check("moe_repack_ep_to_tp", st)
+
+
+def moe_repack_tp_to_ep(src13, src2, P, w13_ep, w2_ep, stream=None):
+    """Rebuild whole experts w13_ep (E_l, 2I, H), w2_ep (E_l, H, I) from the P
+    TP-slice blocks src13[q] (E_l, 2I/P, H), src2[q] (E_l, H, I/P)."""
+    E_l, two_i, H = w13_ep.shape
+    I = two_i // 2
+    if len(src13) != P or len(src2) != P:
+        raise ValueError("need P source blocks for each tensor")
+    Ip = I // P
+    arr13 = (_p * P)(*[_ptr(b, f"src13[{q}]", w13_ep.dtype, (E_l, 2 * Ip, H)) for q, b in enumerate(src13)])
+    arr2 = (_p * P)(*[_ptr(b, f"src2[{q}]", w13_ep.dtype, (E_l, H, Ip)) for q, b in enumerate(src2)])
+    st = lib().moe_repack_tp_to_ep(
+        arr13, arr2, E_l, H, I, P, _dtype_code(w13_ep), _ptr(w13_ep, "w13_ep"),
+        _ptr(w2_ep, "w2_ep", w13_ep.dtype, (E_l, H, I)), _stream(stream))
+    _check("moe_repack_tp_to_ep", st)

@@ -25,7 +25,7 @@ using namespace moe;
 
 namespace {
 
-constexpr int ABI_VERSION = 3;
+constexpr int ABI_VERSION = 4;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -214,8 +214,9 @@ int moe_combine(const void* y_pair, const int32_t* pair_pos, const float* topk_w
   return launched();
 }
 
-int moe_repack_ep_to_tp(const void* w13_ep, const void* w2_ep, int E_local, int H, int I, int P,
-                        int dtype, void* const* dst13, void* const* dst2, hipStream_t stream) {
+namespace {
+
+int check_repack(int E_local, int H, int I, int P, int dtype) {
   if (E_local < 1 || H < 1 || I < 1 || P < 1 || !dtype_ok(dtype)) return MOE_EINVAL;
   if (I % P != 0) return MOE_EINVAL;
   if (P > MAX_P) return MOE_EUNSUPPORTED;
@@ -223,14 +224,42 @@ int moe_repack_ep_to_tp(const void* w13_ep, const void* w2_ep, int E_local, int 
   if ((static_cast<long long>(I / P) * eb) % 16 != 0 || (static_cast<long long>(H) * eb) % 16 != 0)
     return MOE_EUNSUPPORTED;
   if (!repack_fits(E_local, H, I, dtype)) return MOE_EUNSUPPORTED;
-  if (!w13_ep || !w2_ep || !dst13 || !dst2 || !aligned16(w13_ep) || !aligned16(w2_ep)) return MOE_EINVAL;
-  PeerPtrs d13{}, d2{};
+  return MOE_OK;
+}
+
+int gather_blocks(int P, void* const* p13, void* const* p2, PeerPtrs& b13, PeerPtrs& b2) {
+  if (!p13 || !p2) return MOE_EINVAL;
   for (int q = 0; q < P; ++q) {
-    if (!dst13[q] || !dst2[q] || !aligned16(dst13[q]) || !aligned16(dst2[q])) return MOE_EINVAL;
-    d13.p[q] = dst13[q];
-    d2.p[q] = dst2[q];
+    if (!p13[q] || !p2[q] || !aligned16(p13[q]) || !aligned16(p2[q])) return MOE_EINVAL;
+    b13.p[q] = p13[q];
+    b2.p[q] = p2[q];
   }
+  return MOE_OK;
+}
+
+}  // namespace
+
+int moe_repack_ep_to_tp(const void* w13_ep, const void* w2_ep, int E_local, int H, int I, int P,
+                        int dtype, void* const* dst13, void* const* dst2, hipStream_t stream) {
+  int st = check_repack(E_local, H, I, P, dtype);
+  if (st != MOE_OK) return st;
+  if (!w13_ep || !w2_ep || !aligned16(w13_ep) || !aligned16(w2_ep)) return MOE_EINVAL;
+  PeerPtrs d13{}, d2{};
+  st = gather_blocks(P, dst13, dst2, d13, d2);
+  if (st != MOE_OK) return st;
   launch_repack_ep_to_tp(dtype, w13_ep, w2_ep, E_local, H, I, P, d13, d2, stream);
+  return launched();
+}
+
+int moe_repack_tp_to_ep(const void* const* src13, const void* const* src2, int E_local, int H, int I, int P,
+                        int dtype, void* w13_ep, void* w2_ep, hipStream_t stream) {
+  int st = check_repack(E_local, H, I, P, dtype);
+  if (st != MOE_OK) return st;
+  if (!w13_ep || !w2_ep || !aligned16(w13_ep) || !aligned16(w2_ep)) return MOE_EINVAL;
+  PeerPtrs s13{}, s2{};
+  st = gather_blocks(P, const_cast<void* const*>(src13), const_cast<void* const*>(src2), s13, s2);
+  if (st != MOE_OK) return st;
+  launch_repack_tp_to_ep(dtype, s13, s2, E_local, H, I, P, w13_ep, w2_ep, stream);
   return launched();
 }
 

@@ -74,5 +74,8 @@ struct PeerPtrs {
 bool repack_fits(int E_local, int H, int I, int dtype);
 void launch_repack_ep_to_tp(int dtype, const void* w13, const void* w2, int E_local, int H, int I,
                             int P, const PeerPtrs& d13, const PeerPtrs& d2, hipStream_t s);
+// TP -> EP: gather the P blocks back into whole experts (exact inverse)
+void launch_repack_tp_to_ep(int dtype, const PeerPtrs& s13, const PeerPtrs& s2, int E_local, int H, int I, int P,
+                            void* w13, void* w2, hipStream_t s);
 
 }  // namespace moe

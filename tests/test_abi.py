@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_repack_ep_to_tp"):
+    for n in ("moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_repack_ep_to_tp",
+              "moe_repack_tp_to_ep"):
         assert n in names
 
 
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
     for s in range(5):
         assert L.moe_status_str(s).decode().startswith(
             ["MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP"][s])
@@ -197,3 +198,16 @@ def test_repack_rejects(L):
     assert L.moe_repack_ep_to_tp(FAKE, FAKE, 2, 256, 128, 2, BF16, ptrs(FAKE, MISALIGNED), d,
                                  None) == MOE_EINVAL
     assert L.moe_repack_ep_to_tp(None, FAKE, 2, 256, 128, 2, BF16, d, d, None) == MOE_EINVAL
+
+
+def test_repack_tp_to_ep_rejects(L):
+    d = ptrs(FAKE, FAKE)
+    assert L.moe_repack_tp_to_ep(d, d, 2, 256, 100, 3, BF16, FAKE, FAKE, None) == MOE_EINVAL  # I % P
+    assert L.moe_repack_tp_to_ep(d, d, 2, 256, 128, 0, BF16, FAKE, FAKE, None) == MOE_EINVAL
+    assert L.moe_repack_tp_to_ep(d, d, 2, 256, 8 * 65, 65, BF16, FAKE, FAKE, None) == MOE_EUNSUPPORTED
+    assert L.moe_repack_tp_to_ep(d, d, 2, 256, 12, 2, BF16, FAKE, FAKE, None) == MOE_EUNSUPPORTED  # 6*2 B
+    assert L.moe_repack_tp_to_ep(ptrs(FAKE, None), d, 2, 256, 128, 2, BF16, FAKE, FAKE, None) == MOE_EINVAL
+    assert L.moe_repack_tp_to_ep(d, ptrs(MISALIGNED, FAKE), 2, 256, 128, 2, BF16, FAKE, FAKE, None) == MOE_EINVAL
+    assert L.moe_repack_tp_to_ep(None, d, 2, 256, 128, 2, BF16, FAKE, FAKE, None) == MOE_EINVAL
+    assert L.moe_repack_tp_to_ep(d, d, 2, 256, 128, 2, BF16, None, FAKE, None) == MOE_EINVAL
+    assert L.moe_repack_tp_to_ep(d, d, 2, 256, 128, 2, BF16, FAKE, MISALIGNED, None) == MOE_EINVAL

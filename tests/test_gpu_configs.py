@@ -69,7 +69,7 @@ def test_qwen3_235b_tp_share(B, routing):
     run_case("qwen3_235b_tp", B, routing)
 
 
-def test_qwen3_235b_repack_ep_to_tp_bit_exact():
+def test_qwen3_235b_repack_both_directions_bit_exact():
     import torch
 
     import gpu_helpers as gh
@@ -91,3 +91,10 @@ def test_qwen3_235b_repack_ep_to_tp_bit_exact():
     for q in range(P):
         assert np.array_equal(gh.from_dev(d13[q]), b13[q]), f"W13 block {q}"
         assert np.array_equal(gh.from_dev(d2[q]), b2[q]), f"W2 block {q}"
+    # the switch back: the GPU's own blocks gathered into whole experts again
+    print(f"[case] repack TP->EP E_local={E_l} H={cfg.H} I={cfg.I} P={P}", flush=True)
+    r13, r2 = torch.empty_like(w13), torch.empty_like(w2)
+    moe_layer_amd.moe_repack_tp_to_ep(d13, d2, P, r13, r2)
+    torch.cuda.synchronize()
+    assert np.array_equal(gh.from_dev(r13), r["w13_ep"]), "W13 round trip"
+    assert np.array_equal(gh.from_dev(r2), r["w2_ep"]), "W2 round trip"

@@ -196,6 +196,15 @@ def test_repack_small(dtype, P, E_l, H, I):
     for q in range(P):
         assert np.array_equal(gh.from_dev(d13[q]), b13[q])
         assert np.array_equal(gh.from_dev(d2[q]), b2[q])
+    # the inverse from the oracle's blocks rebuilds the experts the oracle
+    # rebuilds (the originals), byte for byte
+    r13 = torch.empty((E_l, 2 * I, H), dtype=tdt, device="cuda")
+    r2 = torch.empty((E_l, H, I), dtype=tdt, device="cuda")
+    moe_layer_amd.moe_repack_tp_to_ep([gh.to_dev(b) for b in b13], [gh.to_dev(b) for b in b2], P, r13, r2)
+    torch.cuda.synchronize()
+    o13, o2 = oracle.repack_tp_to_ep(b13, b2)
+    assert np.array_equal(gh.from_dev(r13), o13) and np.array_equal(gh.from_dev(r2), o2)
+    assert np.array_equal(o13, w13) and np.array_equal(o2, w2)
 
 
 @pytest.mark.parametrize("routing", ["uniform", "zipf"])
