@@ -97,7 +97,7 @@ def parse():
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("expert_gemm.hip", "common.hpp"):
+    for f in ("expert_gemm.hip", "expert_tile.hip", "common.hpp", "moe_internal.h"):
         with open(os.path.join(ROOT, "moe_layer_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
