@@ -16,6 +16,9 @@ values; bf16 inputs are widened exactly, nothing is rounded in between):
   per destination -- Moebius review, §3.1 and Fig. 4.
 * the argsort of tokens by expert -- Sem-MoE notes, Key design 4 (the argsort
   kernel used to reorder tokens).
+* the EP token exchange: each token goes to the GPU that owns its expert and
+  its result comes back -- Moebius review, problem definition (EP layout), and
+  Sem-MoE notes, motivation (two all-to-alls per MoE layer).
 
 Readings where the pages are silent (each one is also a test pin):
 
@@ -33,6 +36,12 @@ Readings where the pages are silent (each one is also a test pin):
 * No capacity limit: every picked (token, expert) pair is computed.
 * The EP and TP outputs are partial sums: the EP rank adds only its local
   experts' terms; the TP rank adds every term restricted to its I-slice.
+* EP dispatch: one send row per routed (token, slot) pair, grouped by the
+  rank d = id // E_local that owns the expert, ascending pair index inside a
+  group (a token picking two experts of one rank is sent twice; shared
+  experts, ids >= E, stay local and are not sent).  The receiver answers with
+  one unweighted expert-output row per received row, in arrival order (sender
+  0's rows first); the sender applies its own routing weights when it sums.
 """
 import numpy as np
 
@@ -40,6 +49,7 @@ __all__ = [
     "widen", "gate_logits", "softmax_rows", "topk_desc", "route", "local_ids",
     "permute", "silu", "expert_ffn", "grouped_ffn", "combine", "moe_layer",
     "tp_slice", "repack_ep_to_tp", "repack_tp_to_ep", "brute_force_layer",
+    "dispatch", "ep_exchange_layer",
 ]
 
 
@@ -254,6 +264,68 @@ def repack_tp_to_ep(blocks13, blocks2):
     gate = np.concatenate([b[:, :Ip, :] for b in blocks13], axis=1)
     up = np.concatenate([b[:, Ip:, :] for b in blocks13], axis=1)
     return np.concatenate([gate, up], axis=1), np.concatenate(list(blocks2), axis=2)
+
+
+def dispatch(x, ids, E_local: int, P: int) -> dict:
+    """Send side of the EP dispatch on one rank (Moebius review, problem
+    definition: tokens reach the GPU that owns their expert by an all-to-all).
+
+    Pair p = t * kk + j goes to rank ids[p] // E_local when that is < P.  The
+    send layout is the stable argsort of the pairs by destination rank (the
+    expert argsort above with the rank as the key): block r of the send buffer
+    holds rank r's rows, ascending pair index.  Returns counts (P), offsets
+    (P + 1), send_order (n_sent pair ids), pair_pos (T * kk, -1 if not sent),
+    send_x (n_sent, H) exact copies of x[send_order // kk] and send_ids
+    (n_sent) the global expert id of each row.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    kk = ids.shape[1]
+    counts, offsets, send_order, pair_pos = permute(ids // E_local, 0, P)
+    send_x = np.asarray(x)[send_order.astype(np.int64) // kk]
+    send_ids = ids.ravel()[send_order].astype(np.int32)
+    return {"counts": counts, "offsets": offsets, "send_order": send_order,
+            "pair_pos": pair_pos, "send_x": send_x, "send_ids": send_ids}
+
+
+def ep_exchange_layer(x_shares, w_gate, gate_bias, w13, w2, k: int, renorm: bool) -> dict:
+    """The EP layer across P ranks with both exchanges written out.
+
+    x_shares[q] is rank q's own tokens; P = len(x_shares) ranks, rank r owns
+    whole experts [r E/P, (r+1) E/P) of w13 (E, 2I, H) / w2 (E, H, I).  Every
+    rank routes its tokens and dispatches them; rank r takes block r of every
+    sender in sender order, evaluates each received row with the expert its id
+    names, and sends the unweighted outputs back in arrival order; sender q
+    sums them per token with its routing weights in slot order.  Returns the
+    per-rank outputs y (list) and the per-rank dispatch results.
+    """
+    P = len(x_shares)
+    E = np.asarray(w_gate).shape[0]
+    E_l = E // P
+    H = np.asarray(x_shares[0]).shape[1]
+    routed, sends = [], []
+    for q in range(P):
+        ids, w = route(gate_logits(x_shares[q], w_gate, gate_bias), k, renorm)
+        routed.append((ids, w))
+        sends.append(dispatch(x_shares[q], ids, E_l, P))
+    back = [[None] * P for _ in range(P)]          # back[q][r]: rows rank r returns to q
+    for r in range(P):
+        parts = [(s["offsets"][r], s["offsets"][r + 1]) for s in sends]
+        rx = np.concatenate([widen(s["send_x"][a:b]) for s, (a, b) in zip(sends, parts)])
+        rid = np.concatenate([s["send_ids"][a:b] for s, (a, b) in zip(sends, parts)])
+        ry = np.zeros((rx.shape[0], H))
+        for e in np.unique(rid):
+            rows = np.nonzero(rid == e)[0]
+            _, ry[rows] = expert_ffn(rx[rows], w13[e], w2[e])
+        start = 0
+        for q, (a, b) in enumerate(parts):
+            back[q][r] = ry[start:start + (b - a)]
+            start += b - a
+    ys = []
+    for q in range(P):
+        ids, w = routed[q]
+        recv = np.concatenate(back[q], axis=0)     # rank order = send order
+        ys.append(combine(recv, sends[q]["pair_pos"], w, ids.shape[0], ids.shape[1]))
+    return {"y": ys, "dispatch": sends, "routed": routed}
 
 
 def brute_force_layer(x, w_gate, gate_bias, w13, w2, k: int, renorm: bool,

@@ -297,6 +297,66 @@ def test_repack_block_equals_tp_view_of_local_experts():
         assert np.array_equal(b2[q], t2[r * E_l:(r + 1) * E_l])
 
 
+# ---------------------------------------------------------------- P11 EP dispatch
+
+@pytest.mark.parametrize("E_l,P", [(2, 4), (3, 3), (1, 8), (8, 1)])
+def test_dispatch_is_the_stable_argsort_by_rank(E_l, P):
+    rng = np.random.default_rng(21)
+    T, kk, H = 29, 3, 5
+    E = E_l * P
+    ids = rng.integers(0, E + 2, size=(T, kk)).astype(np.int32)   # ids >= E: shared, stay local
+    x = rng.integers(0, 60000, size=(T, H)).astype(np.uint16)
+    d = oracle.dispatch(x, ids, E_l, P)
+    flat = ids.ravel().astype(np.int64)
+    dest = flat // E_l
+    sent = flat < E
+    idx = np.nonzero(sent)[0]
+    want = idx[np.argsort(dest[idx], kind="stable")]
+    assert d["send_order"].tolist() == want.tolist()
+    assert d["counts"].tolist() == np.bincount(dest[idx], minlength=P).tolist()
+    assert d["offsets"].tolist() == [0] + np.cumsum(d["counts"]).tolist()
+    assert (d["pair_pos"][want] == np.arange(want.size)).all()
+    assert (d["pair_pos"][~sent] == -1).all()
+    assert np.array_equal(d["send_x"], x[want // kk])
+    assert d["send_x"].dtype == x.dtype
+    assert d["send_ids"].tolist() == flat[want].tolist()
+    for r in range(P):
+        blk = d["send_ids"][d["offsets"][r]:d["offsets"][r + 1]]
+        assert ((blk >= r * E_l) & (blk < (r + 1) * E_l)).all()
+
+
+def test_dispatch_hand_example():
+    # T=3, kk=2, two ranks of two experts: ids (3,0), (1,2), (2,3)
+    # -> ranks (1,0), (0,1), (1,1): rank 0 gets pairs 1, 2; rank 1 gets 0, 3, 4, 5
+    x = np.array([[10.0], [20.0], [30.0]])
+    d = oracle.dispatch(x, np.array([[3, 0], [1, 2], [2, 3]]), 2, 2)
+    assert d["counts"].tolist() == [2, 4]
+    assert d["offsets"].tolist() == [0, 2, 6]
+    assert d["send_order"].tolist() == [1, 2, 0, 3, 4, 5]
+    assert d["pair_pos"].tolist() == [2, 0, 1, 3, 4, 5]
+    assert d["send_x"][:, 0].tolist() == [10.0, 20.0, 10.0, 20.0, 30.0, 30.0]
+    assert d["send_ids"].tolist() == [0, 1, 3, 2, 2, 3]
+
+
+@pytest.mark.parametrize("P,routing", [(2, "uniform"), (4, "zipf"), (8, "uniform")])
+def test_ep_exchange_equals_full_layer(P, routing):
+    # P ranks each own T/P tokens; after dispatch, expert work and return the
+    # concatenated outputs are the full layer on the whole batch.
+    cfg = small_cfg(E=8, I=24, H=32, k=3, T=24)
+    m = make_full_model(cfg, 24, routing=routing, seed=13)
+    shares = np.split(m["x"], P)
+    ex = oracle.ep_exchange_layer(shares, m["w_gate"], m["gate_bias"], m["w13"], m["w2"],
+                                  cfg.k, cfg.renorm)
+    full = oracle.moe_layer(m["x"], m["w_gate"], m["gate_bias"], m["w13"], m["w2"], cfg.k, cfg.renorm)
+    assert rel_err(np.concatenate(ex["y"]), full["y"]) < REL
+    yb = oracle.brute_force_layer(m["x"], m["w_gate"], m["gate_bias"], m["w13"], m["w2"],
+                                  cfg.k, cfg.renorm)
+    assert rel_err(np.concatenate(ex["y"]), yb) < REL
+    # every pair is sent exactly once, to the rank owning its expert
+    n_pairs = sum(s["offsets"][-1] for s in ex["dispatch"])
+    assert n_pairs == m["x"].shape[0] * cfg.k
+
+
 # ---------------------------------------------------------------- P10 silu
 
 def test_silu_closed_forms():
