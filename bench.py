@@ -3,6 +3,8 @@ the dominant kernel and the CPU oracle timed beside it.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME --tokens T --routing R]
     python bench.py --sweep --out results.jsonl     # every batch of the EP/TP/30B workloads
+    python bench.py --workload repack               # EP<->TP expert-weight repack
+    python bench.py --workload dispatch [--tokens T] # EP dispatch send layout + return combine
 
 A step is one pass of the whole hot path (gate GEMM + softmax/top-k + permute
 in one launch, expert up-projection with SiLU*up, down-projection, combine:
@@ -77,6 +79,111 @@ def bench_repack(steps, warmup):
                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None},
         "tp_to_ep": {"ms_per_step": t_back * 1e3, "achieved_GBs": gbs_back,
                      "frac": gbs_back / HBM_PEAK_GBS},
+    }
+
+
+def bench_dispatch(steps, warmup, T_main, routing, cpu=True):
+    """EP dispatch send side on one Qwen3-235B-shaped EP rank (P = 8, 16
+    experts per rank, H = 4096, top-8): pairs sorted by owning rank and their
+    token rows copied into the send buffer (moe_dispatch: two launches), and
+    the return leg beside it (moe_combine of the returned rows with the
+    dispatch's pair positions and the routing weights).  T is this rank's own
+    (data-parallel) tokens; the routing table is a seeded draw.  Each call is
+    timed inside a replayed HIP graph of 20 calls."""
+    import numpy as np
+    import torch
+
+    import moe_layer_amd as M
+    from moe_inputs import get_config
+    from moe_inputs.gen import make_x, routing_table
+    cfg = get_config("qwen3_235b_ep")
+    P, E_l, H, k = cfg.P, cfg.E // cfg.P, cfg.H, cfg.k
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    def one(T):
+        xh, idh = make_x(cfg, T, T_draw=T), routing_table(cfg, T, routing)
+        x, ids = dev(xh), dev(idh)
+        w = torch.rand((T, k), dtype=torch.float32, device="cuda")
+        n = T * k
+        i32 = lambda m: torch.empty(m, dtype=torch.int32, device="cuda")
+        counts, offsets, order, pos, sids = i32(P), i32(P + 1), i32(n), i32(n), i32(n)
+        send_x = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        go = lambda: M.moe_dispatch(x, ids, E_l, P, counts, offsets, order, pos, send_x, sids)
+        back = lambda: M.moe_combine(send_x, pos, w, y)   # returned rows stand in for expert outputs
+
+        def timed(fn, reps=20):
+            """Mean time per call: `reps` calls captured in one HIP graph,
+            replayed `steps` times between two events on the replay stream
+            (the calls are a few microseconds each; replay keeps the host's
+            launch cost out of the figure)."""
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    fn()
+            for _ in range(max(1, warmup)):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e-3 / (steps * reps)
+
+        t_d, t_c = timed(go), timed(back)
+        n_sent = int(offsets[-1].item())
+        bytes_d = 2 * H * (T + n_sent) + 4 * (2 * T * k + 2 * n_sent)
+        bytes_c = 2 * H * (n_sent + T) + 8 * T * k
+        return {"T": T, "n_sent": n_sent, "dispatch_us": t_d * 1e6, "dispatch_GBs": bytes_d / t_d / 1e9,
+                "dispatch_bytes": bytes_d, "return_combine_us": t_c * 1e6,
+                "return_combine_GBs": bytes_c / t_c / 1e9, "host": (xh, idh)}
+
+    rows = [one(T) for T in sorted({32, 256, 1024, 2048, T_main})]
+    main = next(r for r in rows if r["T"] == T_main)
+    frac = main["dispatch_GBs"] / HBM_PEAK_GBS
+    cpu_line = None
+    if cpu:
+        import oracle
+        xh, idh = main["host"]
+        runs, tot = 0, 0.0
+        while runs == 0 or (tot < 10.0 and runs < 200):
+            t0 = time.perf_counter()
+            oracle.dispatch(xh, idh, E_l, P)
+            tot += time.perf_counter() - t0
+            runs += 1
+        cpu_line = {"value": main["dispatch_bytes"] / (tot / runs) / 1e9, "unit": "GB/s", "cores": 1,
+                    "kind": "oracle", "sample": f"oracle.dispatch on the same T={T_main} rank share, "
+                                                f"{runs} run(s), mean {tot / runs * 1e3:.2f} ms (numpy, one thread)"}
+    for r in rows:
+        r.pop("host")
+    return {
+        "metric": "EP dispatch send-layout throughput (algorithmic HBM bytes / time)",
+        "value": main["dispatch_GBs"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": main["dispatch_us"] * 1e-3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded x, seeded routing table)",
+        "config": {"workload": f"EP dispatch of one Qwen3-235B-A22B-shaped rank share: T={T_main} own "
+                               f"tokens, top-{k} of 128 experts, P={P} ranks of {E_l}, H={H}, {routing}",
+                   "rows_sent": main["n_sent"]},
+        "roofline": {"bound": "hbm", "kernel": "dispatch_kernel (rank counts, ranking and row copy in one launch)",
+                     "achieved": main["dispatch_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": frac, "traffic": None,
+                     "algorithmic_bytes_per_launch": main["dispatch_bytes"]},
+        "by_tokens": [{k2: (round(v, 3) if isinstance(v, float) else v) for k2, v in r.items()}
+                      for r in rows],
+        "cpu_baseline": cpu_line,
     }
 
 
@@ -362,6 +469,11 @@ def main():
 
     if args.workload == "repack":
         print(json.dumps(bench_repack(args.steps, args.warmup)), flush=True)
+        return
+    if args.workload == "dispatch":
+        print(json.dumps(bench_dispatch(args.steps, args.warmup, args.tokens or 256,
+                                        args.routing or "uniform", not args.no_cpu_baseline)),
+              flush=True)
         return
 
     name = args.workload

@@ -11,7 +11,9 @@
  * (token, slot) pairs by expert (moe_permute); the expert FFN
  * W2 (silu(W1 x) * W3 x) on every kept pair (moe_grouped_gemm); the weighted
  * sum per token (moe_combine).  moe_repack_ep_to_tp is the local-permute phase
- * of the EP->TP weight reshard.
+ * of the EP->TP weight reshard.  moe_dispatch packs an EP rank's routed
+ * token rows by destination rank (the all-to-all send layout); moe_combine
+ * un-permutes and sums what comes back.
  *
  * Conventions for every call
  *   - Pointers are DEVICE pointers unless marked "host".  The caller owns every
@@ -171,12 +173,50 @@ int moe_expert_down(const void* a, const int32_t* offsets, int T, int kk, int n_
  *                       topk_w[t*kk+j] * y_pair[pair_pos[t*kk+j]]
  * fp32 accumulation, one rounding to dtype; rows with no held pair are 0.
  * This is the EP rank's partial before the combine all-to-all, or the TP
- * rank's partial before the all-reduce (Moebius review, §2.1).
- *   y_pair (T*kk, H) dtype, pair_pos (T*kk) int32, topk_w (T*kk) fp32,
- *   y (T, H) dtype [out].   Limit: H * sizeof(dtype) a multiple of 16.
+ * rank's partial before the all-reduce (Moebius review, §2.1).  After
+ * moe_dispatch it is the sender's sum of the rows that came back, with the
+ * dispatch's pair_pos.
+ *   y_pair (rows, H) dtype, every pair_pos entry < rows; pair_pos (T*kk)
+ *   int32; topk_w (T*kk) fp32, or NULL for weight 1 on every slot (with
+ *   kk = 1: the un-permute y[t] = y_pair[pair_pos[t]], an exact copy, which
+ *   puts a receiver's expert outputs back in arrival order); y (T, H) dtype
+ *   [out].   Limit: H * sizeof(dtype) a multiple of 16.
  */
 int moe_combine(const void* y_pair, const int32_t* pair_pos, const float* topk_w, int T, int kk, int H,
                 int dtype, void* y, hipStream_t stream);
+
+/*
+ * moe_dispatch -- send side of the EP token exchange (Moebius review, problem
+ * definition: in the EP layout each token reaches the GPU holding its expert
+ * by an all-to-all; Sem-MoE notes, motivation: one all-to-all out, one back).
+ * This rank's T tokens with their routing (T, kk); rank d < P owns experts
+ * [d E_local, (d+1) E_local).  Pair p = t*kk + j is sent to rank
+ * topk_ids[p] / E_local when that is < P (ids at or past P*E_local, e.g.
+ * shared experts, are not sent): one send row per pair, rank blocks in rank
+ * order, ascending pair id inside a block (moe_permute with the rank as key).
+ *   x           (T, H) dtype
+ *   topk_ids    (T, kk) int32, 16-byte aligned (read as 16-byte vectors)
+ *   send_counts (P) int32 [out]      rows for each rank
+ *   send_offsets(P + 1) int32 [out]  exclusive prefix sum; [P] = n_sent
+ *   send_order  (T*kk) int32 [out]   first n_sent: the pair id of each send row
+ *   pair_pos    (T*kk) int32 [out]   send row of each pair, -1 if not sent
+ *   send_x      (T*kk, H) dtype [out]  first n_sent rows: x[send_order[i] / kk],
+ *                                      exact copies
+ *   send_ids    (T*kk) int32 [out]   first n_sent: topk_ids[send_order[i]], the
+ *                                    global expert id the receiver needs
+ * Rank r's block is rows [send_offsets[r], send_offsets[r+1]).  A receiver
+ * concatenates its blocks from ranks 0..P-1, runs moe_permute on the ids with
+ * kk = 1, g_begin = r*E_local, n_groups = E_local, then moe_grouped_gemm, and
+ * moe_combine(kk = 1, topk_w = NULL) to put its outputs back in arrival
+ * order; the sender's moe_combine of the returned rows with this pair_pos and
+ * its topk_w is its output.
+ * Limits: 1 <= kk <= 64; 1 <= P <= 512; E_local >= 1; P * E_local <= 2^31;
+ * H * sizeof(dtype) a multiple of 16.  T == 0 writes zero counts and offsets.
+ * Deterministic.
+ */
+int moe_dispatch(const void* x, const int32_t* topk_ids, int T, int kk, int H, int E_local, int P,
+                 int dtype, int32_t* send_counts, int32_t* send_offsets, int32_t* send_order,
+                 int32_t* pair_pos, void* send_x, int32_t* send_ids, hipStream_t stream);
 
 /*
  * moe_repack_ep_to_tp -- local-permute phase of the EP->TP expert-weight

@@ -28,7 +28,7 @@ import numpy as np
 from .configs import LayerConfig
 
 # tensor ids used as the first spawn-key element
-_X, _W_GATE, _RHO, _W13, _W2, _W13_SHARED, _W2_SHARED, _W13_TP, _W2_TP = range(9)
+_X, _W_GATE, _RHO, _W13, _W2, _W13_SHARED, _W2_SHARED, _W13_TP, _W2_TP, _IDS = range(10)
 
 ZIPF_S = 1.2
 
@@ -117,6 +117,21 @@ def shared_weights(cfg: LayerConfig, seed: int = 0):
     w13 = _stack(seed, _W13_SHARED, idx, (2 * cfg.I, cfg.H), cfg.H ** -0.5, cfg.dtype)
     w2 = _stack(seed, _W2_SHARED, idx, (cfg.H, cfg.I), cfg.I ** -0.5, cfg.dtype)
     return w13, w2
+
+
+def routing_table(cfg: LayerConfig, T: int, routing: str = "uniform", seed: int = 0) -> np.ndarray:
+    """A synthetic routing table (T, k + n_shared) int32 for the steps after
+    the gate: per token, k distinct routed ids drawn without replacement with
+    probabilities proportional to exp(gate bias) (uniform, or the Zipf prior
+    above), then the shared ids E, E+1, ...  Draws only; no gate involved."""
+    prior = np.exp(gate_bias(cfg, routing, seed).astype(np.float64))
+    prior /= prior.sum()
+    rng = _rng(seed, _IDS, T)
+    ids = np.empty((T, cfg.kk), dtype=np.int32)
+    for t in range(T):
+        ids[t, :cfg.k] = rng.choice(cfg.E, size=cfg.k, replace=False, p=prior)
+    ids[:, cfg.k:] = cfg.E + np.arange(cfg.n_shared, dtype=np.int32)
+    return ids
 
 
 def make_layer_inputs(cfg: LayerConfig, T: int, routing: str = "uniform", seed: int = 0,

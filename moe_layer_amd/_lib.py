@@ -22,7 +22,7 @@ MOE_OP_EXPERT_UP, MOE_OP_EXPERT_DOWN = 5, 6
 EXPORTED = (
     "moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes",
     "moe_route", "moe_route_permute", "moe_permute", "moe_grouped_gemm", "moe_expert_up",
-    "moe_expert_down", "moe_combine", "moe_repack_ep_to_tp", "moe_repack_tp_to_ep",
+    "moe_expert_down", "moe_combine", "moe_repack_ep_to_tp", "moe_repack_tp_to_ep", "moe_dispatch",
 )
 
 
@@ -71,6 +71,8 @@ def lib():
     L.moe_expert_down.argtypes = [_p, _p, _i, _i, _i, _p, _i, _i, _i, _p, _p, _sz, _p]
     L.moe_combine.restype = _i
     L.moe_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p]
+    L.moe_dispatch.restype = _i
+    L.moe_dispatch.argtypes = [_p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
     L.moe_repack_ep_to_tp.restype = _i
     L.moe_repack_ep_to_tp.argtypes = [_p, _p, _i, _i, _i, _i, _i, ctypes.POINTER(_p),
                                       ctypes.POINTER(_p), _p]
@@ -224,13 +226,32 @@ def moe_expert_down(a, offsets, T, kk, w2, y_pair, ws, stream=None):
 
 
 def moe_combine(y_pair, pair_pos, topk_w, y, stream=None):
+    """topk_w (T, kk) fp32, or None for weight 1 on every slot (then kk is
+    pair_pos.numel() // T; kk = 1 is the un-permute y[t] = y_pair[pair_pos[t]])."""
     T, H = y.shape
-    kk = topk_w.shape[1]
+    kk = topk_w.shape[1] if topk_w is not None else (pair_pos.numel() // T if T else 1)
     st = lib().moe_combine(
         _ptr(y_pair, "y_pair", y.dtype), _ptr(pair_pos, "pair_pos", torch.int32, (T * kk,)),
         _ptr(topk_w, "topk_w", torch.float32, (T, kk)), T, kk, H, _dtype_code(y), _ptr(y, "y"),
         _stream(stream))
     _check("moe_combine", st)
+
+
+def moe_dispatch(x, topk_ids, E_local, P, send_counts, send_offsets, send_order, pair_pos, send_x,
+                 send_ids, stream=None):
+    """Send layout of the EP dispatch: pairs by owning rank topk_ids // E_local
+    (< P), send_x[i] = x[send_order[i] // kk], send_ids[i] = topk_ids[send_order[i]]."""
+    T, H = x.shape
+    kk = topk_ids.shape[1]
+    st = lib().moe_dispatch(
+        _ptr(x, "x"), _ptr(topk_ids, "topk_ids", torch.int32, (T, kk)), T, kk, H, E_local, P,
+        _dtype_code(x), _ptr(send_counts, "send_counts", torch.int32, (P,)),
+        _ptr(send_offsets, "send_offsets", torch.int32, (P + 1,)),
+        _ptr(send_order, "send_order", torch.int32, (T * kk,)),
+        _ptr(pair_pos, "pair_pos", torch.int32, (T * kk,)),
+        _ptr(send_x, "send_x", x.dtype, (T * kk, H)),
+        _ptr(send_ids, "send_ids", torch.int32, (T * kk,)), _stream(stream))
+    _check("moe_dispatch", st)
 
 
 def moe_repack_ep_to_tp(w13_ep, w2_ep, P, dst13, dst2, stream=None):

@@ -3,6 +3,11 @@
 // (pos = -1).  Accumulation in fp32, one rounding to the output type.  In the
 // EP view this is the rank's partial before the combine all-to-all; in the TP
 // view it is the partial before the all-reduce (Moebius review, §2.1 and §3.1).
+// After an EP dispatch the sender runs it on the rows that came back, with the
+// dispatch's pair positions.  Without weights (w == nullptr) every weight is 1;
+// with kk = 1 that is the receiver's un-permute of its expert outputs back to
+// arrival order.  The first held slot initialises the sum, so one slot of
+// weight 1 copies its row exactly (signed zeros included).
 //
 // Each thread owns one 16-byte vector of one token row; the slot positions and
 // weights of that token are block-uniform.
@@ -25,14 +30,19 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const T* __res
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+  bool first = true;
   for (int j = 0; j < kk; ++j) {
     const int pos = pair_pos[static_cast<size_t>(t) * kk + j];
     if (pos < 0) continue;
-    const float wj = w[static_cast<size_t>(t) * kk + j];
+    const float wj = w ? w[static_cast<size_t>(t) * kk + j] : 1.f;
     const uint4 v = ld16(y_pair + static_cast<size_t>(pos) * H + h0);
     const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] += wj * Elem<T>::load(e + i);
+    for (int i = 0; i < VEC; ++i) {
+      const float term = wj * Elem<T>::load(e + i);
+      acc[i] = first ? term : acc[i] + term;
+    }
+    first = false;
   }
   T* dst = y + static_cast<size_t>(t) * H + h0;
 #pragma unroll

@@ -25,7 +25,7 @@ using namespace moe;
 
 namespace {
 
-constexpr int ABI_VERSION = 4;
+constexpr int ABI_VERSION = 5;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -208,9 +208,29 @@ int moe_combine(const void* y_pair, const int32_t* pair_pos, const float* topk_w
   if (T < 0 || kk < 1 || kk > MAX_KK || H < 1 || !dtype_ok(dtype)) return MOE_EINVAL;
   if ((static_cast<long long>(H) * elem_bytes(dtype)) % 16 != 0) return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!y_pair || !pair_pos || !topk_w || !y) return MOE_EINVAL;
-  if (!aligned16(y_pair) || !aligned16(y) || !aligned4(pair_pos) || !aligned4(topk_w)) return MOE_EINVAL;
+  if (!y_pair || !pair_pos || !y) return MOE_EINVAL;
+  if (!aligned16(y_pair) || !aligned16(y) || !aligned4(pair_pos) || (topk_w && !aligned4(topk_w)))
+    return MOE_EINVAL;
   launch_combine(dtype, y_pair, pair_pos, topk_w, T, kk, H, y, stream);
+  return launched();
+}
+
+int moe_dispatch(const void* x, const int32_t* topk_ids, int T, int kk, int H, int E_local, int P,
+                 int dtype, int32_t* send_counts, int32_t* send_offsets, int32_t* send_order,
+                 int32_t* pair_pos, void* send_x, int32_t* send_ids, hipStream_t stream) {
+  if (T < 0 || kk < 1 || kk > MAX_KK || H < 1 || E_local < 1 || P < 1 || !dtype_ok(dtype))
+    return MOE_EINVAL;
+  if (P > MAX_GROUPS || static_cast<long long>(T) * kk > (1LL << 30)) return MOE_EUNSUPPORTED;
+  if (static_cast<long long>(P) * E_local > (1LL << 31)) return MOE_EUNSUPPORTED;
+  if ((static_cast<long long>(H) * elem_bytes(dtype)) % 16 != 0) return MOE_EUNSUPPORTED;
+  if (static_cast<long long>(H) * elem_bytes(dtype) / 16 > (1LL << 30)) return MOE_EUNSUPPORTED;
+  if (!send_counts || !send_offsets || !aligned4(send_counts) || !aligned4(send_offsets)) return MOE_EINVAL;
+  if (T > 0 && (!x || !topk_ids || !send_order || !pair_pos || !send_x || !send_ids || !aligned16(x) ||
+                !aligned16(send_x) || !aligned16(topk_ids) || !aligned4(send_order) ||
+                !aligned4(pair_pos) || !aligned4(send_ids)))
+    return MOE_EINVAL;
+  launch_dispatch(dtype, x, topk_ids, T, kk, H, E_local, P, send_counts, send_offsets, send_order,
+                  pair_pos, send_x, send_ids, stream);
   return launched();
 }
 

@@ -30,6 +30,11 @@ void launch_route(int dtype, const void* x, const void* wg, const float* bias, f
 // counts, offsets, stable permutation
 void launch_permute(const int32_t* ids, int T, int kk, int g_begin, int n_groups, int32_t* counts,
                     int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s);
+// EP dispatch: pairs by owning rank ids / E_local (< P), then the send rows
+// send_x[i] = x[send_order[i] / kk] and send_ids[i] = ids[send_order[i]]
+void launch_dispatch(int dtype, const void* x, const int32_t* ids, int T, int kk, int H, int E_local,
+                     int P, int32_t* counts, int32_t* offsets, int32_t* send_order, int32_t* pair_pos,
+                     void* send_x, int32_t* send_ids, hipStream_t s);
 // expert GEMM workspace (one layout for the up and the down launch): split-item
 // counters + per-wave partials
 size_t expert_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dtype);
@@ -62,7 +67,7 @@ void launch_expert_up_tiles(const void* x, const int32_t* sorted_pair, const int
                             int T, int kk, const void* w13, int H, int I, void* a, void* ws, hipStream_t s);
 void launch_expert_down_tiles(const void* a, const int32_t* offsets, int n_groups, int T, int kk,
                               const void* w2, int H, int I, void* y_pair, void* ws, hipStream_t s);
-// weighted combine -> y (T, H)
+// weighted combine -> y (T, H); w == nullptr: every weight 1
 void launch_combine(int dtype, const void* y_pair, const int32_t* pair_pos, const float* w, int T,
                     int kk, int H, void* y, hipStream_t s);
 

@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_repack_ep_to_tp",
-              "moe_repack_tp_to_ep"):
+              "moe_repack_tp_to_ep", "moe_dispatch"):
         assert n in names
 
 
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
     for s in range(5):
         assert L.moe_status_str(s).decode().startswith(
             ["MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP"][s])
@@ -182,6 +182,38 @@ def test_combine_rejects(L):
     assert L.moe_combine(FAKE, FAKE, FAKE, 4, 2, 260, BF16, FAKE, None) == MOE_EUNSUPPORTED
     assert L.moe_combine(FAKE, None, FAKE, 4, 2, 256, BF16, FAKE, None) == MOE_EINVAL
     assert L.moe_combine(MISALIGNED, FAKE, FAKE, 4, 2, 256, BF16, FAKE, None) == MOE_EINVAL
+    assert L.moe_combine(FAKE, FAKE, MISALIGNED, 4, 2, 256, BF16, FAKE, None) == MOE_EINVAL
+    assert L.moe_combine(FAKE, FAKE, None, 4, 2, 260, BF16, FAKE, None) == MOE_EUNSUPPORTED
+
+
+def disp(L, x=FAKE, ids=FAKE, T=4, kk=2, H=256, E_l=2, P=4, dt=BF16, counts=FAKE, offsets=FAKE,
+         order=FAKE, pos=FAKE, send_x=FAKE, send_ids=FAKE):
+    return L.moe_dispatch(x, ids, T, kk, H, E_l, P, dt, counts, offsets, order, pos, send_x, send_ids,
+                          None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kk=0), MOE_EINVAL),
+    (dict(kk=65), MOE_EINVAL),
+    (dict(E_l=0), MOE_EINVAL),
+    (dict(P=0), MOE_EINVAL),
+    (dict(P=513), MOE_EUNSUPPORTED),
+    (dict(E_l=1 << 30, P=4), MOE_EUNSUPPORTED),   # expert ids past 2^31
+    (dict(T=-1), MOE_EINVAL),
+    (dict(H=0), MOE_EINVAL),
+    (dict(H=260), MOE_EUNSUPPORTED),           # bf16 rows must be whole 16-byte vectors
+    (dict(dt=2), MOE_EINVAL),
+    (dict(counts=None), MOE_EINVAL),
+    (dict(offsets=MISALIGNED), MOE_EINVAL),
+    (dict(x=None), MOE_EINVAL),
+    (dict(x=MISALIGNED), MOE_EINVAL),
+    (dict(send_x=MISALIGNED + 4), MOE_EINVAL),
+    (dict(send_ids=None), MOE_EINVAL),
+    (dict(order=MISALIGNED + 1), MOE_EINVAL),
+    (dict(ids=FAKE + 4), MOE_EINVAL),          # the id sweep reads 16-byte vectors
+])
+def test_dispatch_rejects(L, kw, status):
+    assert disp(L, **kw) == status
 
 
 def ptrs(*vals):

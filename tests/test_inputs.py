@@ -66,3 +66,21 @@ def test_expert_weights_are_the_same_in_every_view(rank):
     assert np.array_equal(ep["w13"], full["w13"][2 * rank:2 * rank + 2])
     rp = make_repack_inputs(cfg, rank=rank)
     assert np.array_equal(rp["w2_ep"], full["w2"][2 * rank:2 * rank + 2])
+
+
+@pytest.mark.parametrize("routing", ["uniform", "zipf"])
+def test_routing_table_is_distinct_seeded_and_skewed(routing):
+    from moe_inputs.gen import routing_table
+    cfg = get_config("dsv2_lite")
+    ids = routing_table(cfg, 500, routing, seed=4)
+    assert ids.shape == (500, cfg.k + cfg.n_shared) and ids.dtype == np.int32
+    routed = ids[:, :cfg.k]
+    assert ((routed >= 0) & (routed < cfg.E)).all()
+    assert all(len(set(r)) == cfg.k for r in routed.tolist())
+    assert (ids[:, cfg.k:] == cfg.E + np.arange(cfg.n_shared)).all()
+    assert np.array_equal(ids, routing_table(cfg, 500, routing, seed=4))
+    hist = np.bincount(routed.ravel(), minlength=cfg.E)
+    if routing == "zipf":
+        assert hist.max() > 4 * np.median(hist)
+    else:
+        assert hist.max() < 2 * hist.mean()
