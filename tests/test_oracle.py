@@ -376,3 +376,73 @@ def test_widen_is_exact_for_bf16():
     assert v.tolist()[:3] == [1.0, -1.0, 3.140625]
     assert v[3] == 0.0 and math.copysign(1.0, v[4]) == -1.0
     assert v[5] == 1.0 + 2.0 ** -7
+
+
+# ---------------------------------------------------------------- P12 switch policy and calibration
+
+HAND_TRACE = [5, 8, 11, 12, 9, 7, 5, 4, 3, 12]
+
+
+def run_policy(trace, **kw):
+    from oracle import switch_policy as sp
+    p = sp.SwitchPolicy(**kw)
+    out = [p.step(float(i + 1), c) for i, c in enumerate(trace)]
+    return out, p
+
+
+def test_policy_hand_trace():
+    # T_h = 10, T_l = 6, W = 3, no cooldown; times 1, 2, ..., 10.
+    # t3: 11 > 10 in TP -> EP.  t4..t7: window means 10.33, 10.67, 9.33, 7 >= 6.
+    # t8: mean(7, 5, 4) = 5.33 < 6 -> TP.  t10: 12 > 10 -> EP.
+    out, p = run_policy(HAND_TRACE, t_high=10, t_low=6, window=3, cooldown_s=0)
+    assert out == [0, 0, 1, 0, 0, 0, 0, 2, 0, 1]
+    assert p.mode == 1
+
+
+def test_policy_cooldown_blocks_decisions():
+    # C = 6: after the switch at t3 nothing is decided before t9; at t9 the
+    # window (5, 4, 3) has mean 4 < 6 -> TP; t10 is inside the new cooldown.
+    out, _ = run_policy(HAND_TRACE, t_high=10, t_low=6, window=3, cooldown_s=6)
+    assert out == [0, 0, 1, 0, 0, 0, 0, 0, 2, 0]
+
+
+def test_policy_kv_capacity_veto():
+    # EP holds at most 10 live requests: the switches at t3 (11) and t10 (12)
+    # are cancelled, the first one starting a cooldown of 2 s.
+    out, p = run_policy(HAND_TRACE, t_high=10, t_low=6, window=3, cooldown_s=2, kv_cap_ep=10)
+    assert out == [0, 0, 3, 0, 0, 0, 0, 0, 0, 3]
+    assert p.mode == 0
+    # a capacity that holds the count does not veto
+    out, _ = run_policy(HAND_TRACE, t_high=10, t_low=6, window=3, cooldown_s=0, kv_cap_ep=11)
+    assert out[2] == 1
+
+
+def test_policy_thresholds_are_strict_and_window_must_fill():
+    # rollout setting: T_l = T_h, W = 1
+    out, _ = run_policy([256, 257, 256, 255], t_high=256, t_low=256, window=1, cooldown_s=0)
+    assert out == [0, 1, 0, 2]
+    # EP from the start: no decision until W samples exist
+    out, _ = run_policy([0, 0, 0, 0], t_high=10, t_low=6, window=3, cooldown_s=0, mode=1)
+    assert out == [0, 0, 2, 0]
+
+
+def test_crossover_of_two_lines_is_exact():
+    from oracle import switch_policy as sp
+    B = [8, 16, 32, 64, 128, 256, 512]
+    t_tp = [10 + 0.5 * b for b in B]
+    t_ep = [30 + 0.3 * b for b in B]
+    assert abs(sp.crossover(B, t_tp, t_ep) - 100.0) < 1e-12       # 10 + 0.5B = 30 + 0.3B
+    assert sp.crossover(B, t_ep, t_tp) == 8.0                       # EP faster from the start
+    assert sp.crossover(B, [1.0] * 7, [2.0] * 7) == math.inf        # EP never catches up
+    assert sp.crossover([8, 16], [2.0, 3.0], [3.0, 3.0]) == 16.0    # equal at a grid point
+
+
+def test_simulation_time_and_modes():
+    from oracle import switch_policy as sp
+    p = sp.SwitchPolicy(t_high=10, t_low=6, window=1, cooldown_s=0)
+    step = lambda mode, c: (1.0 if mode == sp.TP else 2.0)
+    r = sp.simulate([5, 20, 20, 1, 1], step, p, switch_time_s=0.5)
+    # TP, TP(->EP after), EP, EP(->TP after), TP
+    assert r["modes"] == [0, 0, 1, 1, 0]
+    assert r["decisions"] == [0, 1, 0, 2, 0]
+    assert r["time"] == 1 + 1 + 0.5 + 2 + 2 + 0.5 + 1
