@@ -5,6 +5,7 @@ the dominant kernel and the CPU oracle timed beside it.
     python bench.py --sweep --out results.jsonl     # every batch of the EP/TP/30B workloads
     python bench.py --workload repack               # EP<->TP expert-weight repack
     python bench.py --workload dispatch [--tokens T] # EP dispatch send layout + return combine
+    python bench.py --workload calibrate --steps 20  # EP/TP crossover across B + switch policy
 
 A step is one pass of the whole hot path (gate GEMM + softmax/top-k + permute
 in one launch, expert up-projection with SiLU*up, down-projection, combine:
@@ -184,6 +185,72 @@ def bench_dispatch(steps, warmup, T_main, routing, cpu=True):
         "by_tokens": [{k2: (round(v, 3) if isinstance(v, float) else v) for k2, v in r.items()}
                       for r in rows],
         "cpu_baseline": cpu_line,
+    }
+
+
+def bench_calibrate(steps, warmup):
+    """The start-up calibration of the EP/TP switch on this GPU: the layer
+    step of one Qwen3-235B-A22B EP rank share and one TP rank share (P = 8,
+    uniform routing) across the global batch B, their crossover
+    (moe_switch_crossover), and the switch policy driven over seeded
+    synthetic load traces with those step times (one layer per iteration;
+    a switch costs one measured EP->TP repack of the layer).  One GPU shows
+    the expert side only: the exchange (all-reduce or all-to-all) and
+    attention, which move the pages' crossover, are not in these times."""
+    import numpy as np
+    import torch
+
+    import moe_layer_amd as M
+    from moe_inputs import get_config
+    from moe_inputs.gen import load_trace
+    batches = list(get_config("qwen3_235b_ep").T_list)
+    t = {"tp": [], "ep": []}
+    for view in ("tp", "ep"):
+        for B in batches:
+            wl = Workload(f"qwen3_235b_{view}", B, "uniform")
+            tm = time_workload(wl, steps, warmup)
+            t[view].append(tm["t_step_s"])
+            del wl
+            torch.cuda.empty_cache()
+    b_star = M.switch_crossover(batches, t["tp"], t["ep"])
+    rep = bench_repack(max(3, steps // 4), 1)
+    switch_s = rep["ms_per_step"] * 1e-3
+    logb = np.log2(np.asarray(batches, dtype=np.float64))
+
+    def step_time(mode, count):
+        x = np.log2(min(max(count, batches[0]), batches[-1]))
+        return float(np.interp(x, logb, t["ep"] if mode == M.MODE_EP else t["tp"]))
+
+    sims = {}
+    for kind, (t_low_f, window) in (("burst", (0.8, 8)), ("rollout", (1.0, 1))):
+        counts, _ = load_trace(kind, 3000, seed=0)
+        out = {}
+        for name, th in (("pages_T_h_256", 256.0), ("calibrated", b_star)):
+            if not math.isfinite(th):
+                continue
+            pol = M.SwitchPolicy(th, t_low_f * th, window, 5e-3)   # cooldown scaled to one-layer steps
+            now, switches = 0.0, 0
+            for c in counts:
+                now += step_time(pol.mode, int(c))
+                d = pol.step(now, int(c))
+                if d in (M.SWITCH_TO_EP, M.SWITCH_TO_TP):
+                    now += switch_s
+                    switches += 1
+            out[name] = {"T_h": th, "time_s": now, "switches": switches}
+        out["always_tp_s"] = sum(step_time(M.MODE_TP, int(c)) for c in counts)
+        out["always_ep_s"] = sum(step_time(M.MODE_EP, int(c)) for c in counts)
+        sims[kind] = out
+    return {
+        "metric": "EP/TP layer-step crossover batch on one GPU (start-up switch calibration)",
+        "value": b_star, "unit": "global batch B", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": None, "higher_is_better": None, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Qwen3-235B-A22B EP and TP rank shares (P = 8), uniform routing, "
+                               "B = 8..2048; policy over seeded burst / rollout load traces"},
+        "layer_step_us": {"B": batches, "tp": [round(v * 1e6, 2) for v in t["tp"]],
+                          "ep": [round(v * 1e6, 2) for v in t["ep"]]},
+        "switch_cost_us": round(switch_s * 1e6, 1),
+        "policy_simulation": sims,
     }
 
 
@@ -469,6 +536,9 @@ def main():
 
     if args.workload == "repack":
         print(json.dumps(bench_repack(args.steps, args.warmup)), flush=True)
+        return
+    if args.workload == "calibrate":
+        print(json.dumps(bench_calibrate(args.steps, args.warmup)), flush=True)
         return
     if args.workload == "dispatch":
         print(json.dumps(bench_dispatch(args.steps, args.warmup, args.tokens or 256,

@@ -251,6 +251,67 @@ int moe_repack_ep_to_tp(const void* w13_ep, const void* w2_ep, int E_local, int 
 int moe_repack_tp_to_ep(const void* const* src13, const void* const* src2, int E_local, int H, int I, int P,
                         int dtype, void* w13_ep, void* w2_ep, hipStream_t stream);
 
+/*
+ * The EP/TP switch policy (Moebius review, §4.5) -- host code, no GPU.
+ * A coordinator calls moe_switch_step once per decode iteration, after the
+ * step, with the global count of in-flight requests:
+ *   - in TP, the mode switches to EP as soon as the count exceeds t_high;
+ *   - in EP, it switches back to TP when the mean of the last `window` counts
+ *     (counts of either mode; none before `window` of them exist) falls below
+ *     t_low; t_low <= t_high is the hysteresis band;
+ *   - after a switch, or a switch cancelled because the target mode's KV
+ *     capacity (live requests it can hold; <= 0: unlimited) is below the
+ *     count, no decision is taken while now_s < that time + cooldown_s.
+ * The caller owns the state (no allocation); calls on one state must not
+ * overlap.  The pages' evaluation uses t_high = 256, cooldown 5 s, and
+ * t_low = 0.8 t_high, window 8 (interactive) or t_low = t_high, window 1
+ * (rollout).
+ */
+#define MOE_SWITCH_WINDOW_MAX 4096
+
+enum moe_mode { MOE_MODE_TP = 0, MOE_MODE_EP = 1 };
+enum moe_switch_decision { MOE_SWITCH_STAY = 0, MOE_SWITCH_TO_EP = 1, MOE_SWITCH_TO_TP = 2,
+                           MOE_SWITCH_VETOED = 3 };
+
+typedef struct moe_switch_params {
+  double t_high;      /* T_h */
+  double t_low;       /* T_l, <= t_high */
+  int window;         /* W, 1 .. MOE_SWITCH_WINDOW_MAX */
+  double cooldown_s;  /* C, >= 0, in the caller's clock */
+  double kv_cap_tp;   /* live requests the TP layout's KV cache holds; <= 0: unlimited */
+  double kv_cap_ep;   /* same for EP */
+} moe_switch_params;
+
+typedef struct moe_switch_state {
+  moe_switch_params p;
+  int mode;                 /* current mode (moe_mode) */
+  int have_last;            /* a switch or cancelled switch has happened */
+  double t_last;            /* its time */
+  long long n_samples;      /* counts seen */
+  int head;                 /* next ring slot (the oldest once the window is full) */
+  long long window_sum;     /* exact sum of the counts in the window */
+  int ring[MOE_SWITCH_WINDOW_MAX];
+} moe_switch_state;
+
+/* Validate p and start in `mode`.  MOE_EINVAL on bad parameters. */
+int moe_switch_init(const moe_switch_params* p, int mode, moe_switch_state* s);
+
+/* Record this iteration's count at time now_s and decide; *decision is a
+ * moe_switch_decision and the state's mode follows it.  MOE_EINVAL on a
+ * negative count, a non-finite time or a null pointer. */
+int moe_switch_step(moe_switch_state* s, double now_s, int in_flight, int* decision);
+
+/*
+ * Start-up calibration of the threshold (Moebius review, §4.5): the batch at
+ * which the EP decode step stops being slower than the TP step.  batches (n,
+ * strictly increasing), t_tp and t_ep (n) are host arrays of measured step
+ * times.  The first i with t_ep[i] <= t_tp[i] gives batches[0] if i == 0, else
+ * the zero of t_ep - t_tp interpolated linearly in the batch between i - 1
+ * and i; if there is none, +infinity.
+ */
+int moe_switch_crossover(const double* batches, const double* t_tp, const double* t_ep, int n,
+                         double* b_star);
+
 #ifdef __cplusplus
 }
 #endif

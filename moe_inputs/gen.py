@@ -28,7 +28,7 @@ import numpy as np
 from .configs import LayerConfig
 
 # tensor ids used as the first spawn-key element
-_X, _W_GATE, _RHO, _W13, _W2, _W13_SHARED, _W2_SHARED, _W13_TP, _W2_TP, _IDS = range(10)
+_X, _W_GATE, _RHO, _W13, _W2, _W13_SHARED, _W2_SHARED, _W13_TP, _W2_TP, _IDS, _TRACE = range(11)
 
 ZIPF_S = 1.2
 
@@ -200,3 +200,48 @@ def make_repack_inputs(cfg: LayerConfig, seed: int = 0, rank: int = 0) -> dict:
     E_l = cfg.E // cfg.P
     w13, w2 = expert_weights(cfg, range(rank * E_l, (rank + 1) * E_l), seed)
     return {"w13_ep": w13, "w2_ep": w2, "rank": rank}
+
+
+def load_trace(kind: str, n: int, seed: int = 0):
+    """A synthetic serving load: the count of in-flight requests at each of n
+    decode iterations, and each iteration's duration in seconds.
+
+    * "burst": online serving with bursts (the bursty serving workload of the
+      Moebius review): a base load of about 60 requests with Poisson noise,
+      and bursts that ramp up to 400-1600 requests over some tens of
+      iterations and drain over a few hundred;
+    * "rollout": RL rollout rounds: each round starts with 1000-2048 requests
+      that finish one by one (geometric lifetimes), a long tail of stragglers
+      at the end of every round;
+    * "noise": a random walk between 0 and 200 requests.
+    Iterations take 20-60 ms.  Draws only; no policy involved.
+    """
+    rng = _rng(seed, _TRACE, {"burst": 0, "rollout": 1, "noise": 2}[kind])
+    if kind == "burst":
+        base = rng.poisson(60, size=n).astype(np.float64)
+        load = base.copy()
+        t = int(rng.integers(100, 300))
+        while t < n:
+            peak = rng.uniform(400, 1600)
+            up, down = int(rng.integers(10, 60)), int(rng.integers(150, 500))
+            shape = np.concatenate([np.linspace(0, 1, up, endpoint=False), np.linspace(1, 0, down)])
+            seg = min(len(shape), n - t)
+            load[t:t + seg] += peak * shape[:seg]
+            t += seg + int(rng.integers(200, 700))
+        counts = np.maximum(load, 0).round().astype(np.int64)
+    elif kind == "rollout":
+        counts = np.zeros(n, dtype=np.int64)
+        t = 0
+        while t < n:
+            start = int(rng.integers(1000, 2049))
+            life = rng.geometric(1.0 / rng.uniform(150, 400), size=start)
+            length = min(int(life.max()) + 1, n - t)
+            steps = np.arange(length)
+            counts[t:t + length] = (life[None, :] > steps[:, None]).sum(axis=1)
+            t += length + int(rng.integers(5, 30))
+    elif kind == "noise":
+        counts = np.clip(np.cumsum(rng.integers(-8, 9, size=n)) + 100, 0, 200).astype(np.int64)
+    else:
+        raise ValueError(f"unknown trace kind {kind!r}")
+    dt = rng.uniform(0.02, 0.06, size=n)
+    return counts, dt

@@ -23,6 +23,7 @@ EXPORTED = (
     "moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes",
     "moe_route", "moe_route_permute", "moe_permute", "moe_grouped_gemm", "moe_expert_up",
     "moe_expert_down", "moe_combine", "moe_repack_ep_to_tp", "moe_repack_tp_to_ep", "moe_dispatch",
+    "moe_switch_init", "moe_switch_step", "moe_switch_crossover",
 )
 
 
@@ -36,6 +37,25 @@ _lib = None
 _p = ctypes.c_void_p
 _i = ctypes.c_int
 _sz = ctypes.c_size_t
+_dp = ctypes.POINTER(ctypes.c_double)
+
+MODE_TP, MODE_EP = 0, 1
+SWITCH_STAY, SWITCH_TO_EP, SWITCH_TO_TP, SWITCH_VETOED = 0, 1, 2, 3
+SWITCH_WINDOW_MAX = 4096
+
+
+class SwitchParams(ctypes.Structure):
+    """moe_switch_params of include/moe.h."""
+    _fields_ = [("t_high", ctypes.c_double), ("t_low", ctypes.c_double), ("window", ctypes.c_int),
+                ("cooldown_s", ctypes.c_double), ("kv_cap_tp", ctypes.c_double),
+                ("kv_cap_ep", ctypes.c_double)]
+
+
+class SwitchState(ctypes.Structure):
+    """moe_switch_state of include/moe.h (caller-owned, fixed size)."""
+    _fields_ = [("p", SwitchParams), ("mode", ctypes.c_int), ("have_last", ctypes.c_int),
+                ("t_last", ctypes.c_double), ("n_samples", ctypes.c_longlong), ("head", ctypes.c_int),
+                ("window_sum", ctypes.c_longlong), ("ring", ctypes.c_int * SWITCH_WINDOW_MAX)]
 
 
 def lib():
@@ -71,6 +91,12 @@ def lib():
     L.moe_expert_down.argtypes = [_p, _p, _i, _i, _i, _p, _i, _i, _i, _p, _p, _sz, _p]
     L.moe_combine.restype = _i
     L.moe_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p]
+    L.moe_switch_init.restype = _i
+    L.moe_switch_init.argtypes = [ctypes.POINTER(SwitchParams), _i, ctypes.POINTER(SwitchState)]
+    L.moe_switch_step.restype = _i
+    L.moe_switch_step.argtypes = [ctypes.POINTER(SwitchState), ctypes.c_double, _i, ctypes.POINTER(_i)]
+    L.moe_switch_crossover.restype = _i
+    L.moe_switch_crossover.argtypes = [_dp, _dp, _dp, _i, _dp]
     L.moe_dispatch.restype = _i
     L.moe_dispatch.argtypes = [_p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
     L.moe_repack_ep_to_tp.restype = _i
@@ -282,3 +308,38 @@ def moe_repack_tp_to_ep(src13, src2, P, w13_ep, w2_ep, stream=None):
         arr13, arr2, E_l, H, I, P, _dtype_code(w13_ep), _ptr(w13_ep, "w13_ep"),
         _ptr(w2_ep, "w2_ep", w13_ep.dtype, (E_l, H, I)), _stream(stream))
     _check("moe_repack_tp_to_ep", st)
+
+
+class SwitchPolicy:
+    """The EP/TP switch coordinator's decision rule (moe_switch_* of the C ABI):
+    one step(now_s, in_flight) per decode iteration."""
+
+    def __init__(self, t_high, t_low, window, cooldown_s, kv_cap_tp=0.0, kv_cap_ep=0.0, mode=MODE_TP):
+        self.params = SwitchParams(float(t_high), float(t_low), int(window), float(cooldown_s),
+                                   float(kv_cap_tp), float(kv_cap_ep))
+        self.state = SwitchState()
+        _check("moe_switch_init", lib().moe_switch_init(ctypes.byref(self.params), int(mode),
+                                                        ctypes.byref(self.state)))
+
+    @property
+    def mode(self):
+        return self.state.mode
+
+    def step(self, now_s, in_flight):
+        d = ctypes.c_int(-1)
+        _check("moe_switch_step", lib().moe_switch_step(ctypes.byref(self.state), float(now_s),
+                                                        int(in_flight), ctypes.byref(d)))
+        return d.value
+
+
+def switch_crossover(batches, t_tp, t_ep):
+    """Batch where the EP step stops being slower than the TP step (linear
+    interpolation between measured batches; inf if never)."""
+    n = len(batches)
+    arr = lambda v: (ctypes.c_double * n)(*[float(x) for x in v])
+    if len(t_tp) != n or len(t_ep) != n:
+        raise ValueError("batches, t_tp and t_ep must have the same length")
+    out = ctypes.c_double(0.0)
+    _check("moe_switch_crossover", lib().moe_switch_crossover(arr(batches), arr(t_tp), arr(t_ep), n,
+                                                              ctypes.byref(out)))
+    return out.value

@@ -1,6 +1,6 @@
 """Build the HIP library libmoe_layer_amd.so in-tree for gfx950.
 
-    python -m moe_layer_amd.build          # compile every csrc/*.hip, link
+    python -m moe_layer_amd.build          # compile every csrc/*.hip and *.cpp, link
 
 Each source compiles to an object in parallel, then one shared library is
 linked next to this file.  Always rebuilds (the sources are few and small).
@@ -34,13 +34,22 @@ CFLAGS = [
 ]
 
 
+# Host-only sources (no device code): plain C++ through the host compiler.
+CXX = os.environ.get("CXX", "g++")
+CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}",
+            "-I/opt/rocm/include", "-D__HIP_PLATFORM_AMD__"]
+
+
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src):
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *CXXFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag; drop that note
     err = "\n".join(line for line in r.stderr.splitlines()

@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_repack_ep_to_tp",
-              "moe_repack_tp_to_ep", "moe_dispatch"):
+              "moe_repack_tp_to_ep", "moe_dispatch", "moe_switch_init", "moe_switch_step",
+              "moe_switch_crossover"):
         assert n in names
 
 
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
     for s in range(5):
         assert L.moe_status_str(s).decode().startswith(
             ["MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP"][s])

@@ -84,3 +84,17 @@ def test_routing_table_is_distinct_seeded_and_skewed(routing):
         assert hist.max() > 4 * np.median(hist)
     else:
         assert hist.max() < 2 * hist.mean()
+
+
+@pytest.mark.parametrize("kind", ["burst", "rollout", "noise"])
+def test_load_traces_are_seeded_and_shaped(kind):
+    from moe_inputs.gen import load_trace
+    c, dt = load_trace(kind, 2000, seed=1)
+    c2, dt2 = load_trace(kind, 2000, seed=1)
+    assert np.array_equal(c, c2) and np.array_equal(dt, dt2)
+    assert c.shape == dt.shape == (2000,) and (c >= 0).all()
+    assert ((dt >= 0.02) & (dt <= 0.06)).all()
+    if kind == "burst":
+        assert np.median(c) < 100 and c.max() > 400
+    if kind == "rollout":
+        assert c.max() >= 1000 and (c == 0).any()
