@@ -11,4 +11,4 @@ Every function here is pinned by a CPU test to something other than itself
 """
 from .moe_oracle import *  # noqa: F401,F403
 from .moe_oracle import __all__  # noqa: F401
-from . import switch_policy  # noqa: F401
+from . import request_schedule, switch_policy  # noqa: F401

@@ -446,3 +446,56 @@ def test_simulation_time_and_modes():
     assert r["modes"] == [0, 0, 1, 1, 0]
     assert r["decisions"] == [0, 1, 0, 2, 0]
     assert r["time"] == 1 + 1 + 0.5 + 2 + 2 + 0.5 + 1
+
+
+# ---------------------------------------------------------------- P13 request scheduling (Attention-DP)
+
+def test_request_scores_hand_example():
+    from oracle import request_schedule as rs
+    # vocabulary of 6 ids in 3 clusters; three requests (the second one empty)
+    cl = [0, 2, 1, 1, 0, 2]
+    tokens = [1, 1, 3, 0, 5, 4, 4, 2]
+    offsets = [0, 5, 5, 8]
+    s = rs.cluster_scores(tokens, offsets, cl, 3)
+    # request 0: ids 1,1,3,0,5 -> clusters 2,2,1,0,2; request 2: ids 4,4,2 -> 0,0,1
+    assert s.tolist() == [[1, 1, 3], [0, 0, 0], [2, 1, 0]]
+    assert rs.affinity_rank(s).tolist() == [2, 0, 0]          # the empty request ties -> 0
+    # group of E = 3: request 0 takes 2, request 1 takes its best free rank 0
+    # (tie among 0 and 1 -> 0), request 2 is left with rank 1
+    assert rs.balanced_ranks(s).tolist() == [2, 0, 1]
+
+
+def test_request_scores_are_bincounts():
+    from oracle import request_schedule as rs
+    rng = np.random.default_rng(5)
+    V, E = 50, 7
+    cl = rng.integers(0, E, size=V)
+    lens = rng.integers(0, 40, size=30)
+    offsets = np.concatenate([[0], np.cumsum(lens)])
+    tokens = rng.integers(0, V, size=offsets[-1])
+    s = rs.cluster_scores(tokens, offsets, cl, E)
+    for r in range(30):
+        seg = tokens[offsets[r]:offsets[r + 1]]
+        assert s[r].tolist() == np.bincount(cl[seg], minlength=E).tolist()
+    assert rs.affinity_rank(s).tolist() == np.argmax(s, axis=1).tolist()   # numpy: first maximum
+
+
+@pytest.mark.parametrize("n,E", [(24, 8), (29, 8), (5, 8), (12, 1)])
+def test_balanced_groups_cover_every_rank(n, E):
+    from oracle import request_schedule as rs
+    rng = np.random.default_rng(n * 10 + E)
+    s = rng.integers(0, 6, size=(n, E))
+    b = rs.balanced_ranks(s)
+    for g0 in range(0, n, E):
+        grp = b[g0:g0 + E].tolist()
+        assert len(set(grp)) == len(grp)                          # distinct inside a group
+        if len(grp) == E:
+            assert sorted(grp) == list(range(E))                  # a full group covers all ranks
+    # the first request of a group always gets its own argmax
+    a = rs.affinity_rank(s)
+    assert (b[::E] == a[::E]).all()
+    # distinct preferences inside every group: balancing changes nothing
+    s2 = np.zeros((n, E), dtype=np.int64)
+    for r in range(n):
+        s2[r, r % E] = 5
+    assert (rs.balanced_ranks(s2) == rs.affinity_rank(s2)).all()
