@@ -6,6 +6,7 @@ the dominant kernel and the CPU oracle timed beside it.
     python bench.py --workload repack               # EP<->TP expert-weight repack
     python bench.py --workload dispatch [--tokens T] # EP dispatch send layout + return combine
     python bench.py --workload calibrate --steps 20  # EP/TP crossover across B + switch policy
+    python bench.py --workload schedule              # Attention-DP request scheduling
 
 A step is one pass of the whole hot path (gate GEMM + softmax/top-k + permute
 in one launch, expert up-projection with SiLU*up, down-projection, combine:
@@ -251,6 +252,76 @@ def bench_calibrate(steps, warmup):
                           "ep": [round(v * 1e6, 2) for v in t["ep"]]},
         "switch_cost_us": round(switch_s * 1e6, 1),
         "policy_simulation": sims,
+    }
+
+
+def bench_schedule(steps, warmup, n_req=2048, E=8, cpu=True):
+    """Attention-DP request scheduling (Sem-MoE notes): 2048 synthetic requests
+    (log-normal lengths, median 300 tokens, 60 % of tokens from a topic
+    cluster) over E = 8 ranks, Qwen3 vocabulary (151 936 ids); one call =
+    per-request cluster counts, argmax ranks and balanced ranks, timed inside
+    a replayed HIP graph of 20 calls."""
+    import numpy as np
+    import torch
+
+    import moe_layer_amd as M
+    from moe_inputs.gen import make_requests
+    tok, off, cl, _ = make_requests(n_req, E, seed=0)
+    t = torch.from_numpy(tok).cuda()
+    o = torch.from_numpy(off).cuda()
+    c = torch.from_numpy(cl).cuda()
+    scores = torch.empty((n_req, E), dtype=torch.int32, device="cuda")
+    aff = torch.empty(n_req, dtype=torch.int32, device="cuda")
+    asg = torch.empty(n_req, dtype=torch.int32, device="cuda")
+    ws = M.schedule_workspace(n_req, E)
+    go = lambda: M.moe_schedule_requests(t, o, c, E, scores, aff, asg, ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        go()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    reps = 20
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            go()
+    for _ in range(max(1, warmup)):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t_call = e0.elapsed_time(e1) * 1e-3 / (steps * reps)
+    n_tok = int(tok.size)
+    nbytes = 4 * n_tok + 4 * cl.size + 4 * (n_req + 1) + 4 * n_req * (E + 2)
+    gbs = nbytes / t_call / 1e9
+    cpu_line = None
+    if cpu:
+        import oracle
+        rs = oracle.request_schedule
+        k = 64
+        t0 = time.perf_counter()
+        sc = rs.cluster_scores(tok[:off[k]], off[:k + 1], cl, E)
+        rs.balanced_ranks(sc)
+        dt = time.perf_counter() - t0
+        cpu_line = {"value": k / dt, "unit": "requests/s", "cores": 1, "kind": "oracle",
+                    "sample": f"oracle cluster_scores + balanced_ranks on the first {k} requests "
+                              f"({int(off[k])} tokens), {dt:.2f} s (pure Python, one thread)"}
+    return {
+        "metric": "Attention-DP request scheduling throughput",
+        "value": n_req / t_call, "unit": "requests/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": t_call * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32", "data": "synthetic (seeded requests and token clusters)",
+        "config": {"workload": f"{n_req} requests, {n_tok} tokens, E = {E} ranks, vocabulary {cl.size}"},
+        "roofline": {"bound": "hbm", "kernel": "schedule_kernel", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "tokens_per_s": n_tok / t_call,
+        "cpu_baseline": cpu_line,
     }
 
 
@@ -536,6 +607,9 @@ def main():
 
     if args.workload == "repack":
         print(json.dumps(bench_repack(args.steps, args.warmup)), flush=True)
+        return
+    if args.workload == "schedule":
+        print(json.dumps(bench_schedule(args.steps, args.warmup, cpu=not args.no_cpu_baseline)), flush=True)
         return
     if args.workload == "calibrate":
         print(json.dumps(bench_calibrate(args.steps, args.warmup)), flush=True)

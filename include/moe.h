@@ -252,6 +252,34 @@ int moe_repack_tp_to_ep(const void* const* src13, const void* const* src2, int E
                         int dtype, void* w13_ep, void* w2_ep, hipStream_t stream);
 
 /*
+ * moe_schedule_requests -- request scheduling under data-parallel attention
+ * (Sem-MoE notes, online data scheduling): with every vocabulary id in one
+ * cluster (= rank), request r goes to S_r = argmax_j sum_{i in r} R_ij, and
+ * every E consecutive requests are spread over all E ranks.
+ *   tokens            (n_tokens) int32   the requests' token ids, concatenated
+ *   req_offsets       (n_req + 1) int32  request r is tokens[req_offsets[r] ..
+ *                                        req_offsets[r+1]) (bounds are clamped
+ *                                        into [0, n_tokens])
+ *   cluster_of_token  (vocab) int32      cluster (rank) of every id, in [0, E)
+ *   scores    (n_req, E) int32 [out]  token positions of r in cluster j (ids
+ *                                     outside [0, vocab), clusters outside
+ *                                     [0, E) are not counted)
+ *   affinity  (n_req) int32 [out]     S_r, ties to the lowest rank
+ *   assigned  (n_req) int32 [out]     balanced rank: requests taken in arrival
+ *             order in groups of E (the last one may be shorter); each takes
+ *             its highest-scoring rank not taken earlier in its group (ties to
+ *             the lowest), so a full group covers every rank once
+ *   ws        >= moe_schedule_workspace_bytes(n_req, E) bytes, zero-filled
+ *             before first use; every completed call leaves it zero.
+ * Limits: 1 <= E <= 64; n_tokens < 2^25.  Deterministic.
+ */
+size_t moe_schedule_workspace_bytes(int n_req, int E);
+int moe_schedule_requests(const int32_t* tokens, int n_tokens, const int32_t* req_offsets, int n_req,
+                          const int32_t* cluster_of_token, int vocab, int E, int32_t* scores,
+                          int32_t* affinity, int32_t* assigned, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
  * The EP/TP switch policy (Moebius review, §4.5) -- host code, no GPU.
  * A coordinator calls moe_switch_step once per decode iteration, after the
  * step, with the global count of in-flight requests:

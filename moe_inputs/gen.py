@@ -28,7 +28,8 @@ import numpy as np
 from .configs import LayerConfig
 
 # tensor ids used as the first spawn-key element
-_X, _W_GATE, _RHO, _W13, _W2, _W13_SHARED, _W2_SHARED, _W13_TP, _W2_TP, _IDS, _TRACE = range(11)
+(_X, _W_GATE, _RHO, _W13, _W2, _W13_SHARED, _W2_SHARED, _W13_TP, _W2_TP, _IDS, _TRACE,
+ _REQ) = range(12)
 
 ZIPF_S = 1.2
 
@@ -245,3 +246,37 @@ def load_trace(kind: str, n: int, seed: int = 0):
         raise ValueError(f"unknown trace kind {kind!r}")
     dt = rng.uniform(0.02, 0.06, size=n)
     return counts, dt
+
+
+def make_requests(n_req: int, E: int, vocab: int = 151936, seed: int = 0, topical: float = 0.6,
+                  median_len: float = 300.0):
+    """Synthetic requests and a token->cluster map for request scheduling.
+
+    * cluster_of_token: the vocabulary split into E equal clusters by a seeded
+      permutation (the co-clustering's output stands in as a random balanced
+      partition);
+    * each request has a topic cluster (uniform) and a length drawn from a
+      log-normal law (median ``median_len``, sigma 1, clipped to 1..8192), a
+      conversational prompt-length mix; each token is, with probability
+      ``topical``, a uniform id of the topic cluster, else a uniform id of
+      the whole vocabulary.
+    Returns tokens (int32, concatenated), offsets (n_req + 1, int32),
+    cluster_of_token (vocab, int32) and the topics (int32).
+    """
+    rng = _rng(seed, _REQ, E)
+    perm = rng.permutation(vocab)
+    cluster = np.empty(vocab, dtype=np.int32)
+    cluster[perm] = (np.arange(vocab) * E // vocab).astype(np.int32)
+    members = [perm[(np.arange(vocab) * E // vocab) == c] for c in range(E)]
+    lens = np.clip(np.round(rng.lognormal(np.log(median_len), 1.0, size=n_req)), 1, 8192).astype(np.int64)
+    topics = rng.integers(0, E, size=n_req).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tokens = np.empty(int(offsets[-1]), dtype=np.int32)
+    for r in range(n_req):
+        n = int(lens[r])
+        own = rng.random(n) < topical
+        mem = members[topics[r]]
+        ids = rng.integers(0, vocab, size=n)
+        ids[own] = mem[rng.integers(0, len(mem), size=int(own.sum()))]
+        tokens[offsets[r]:offsets[r + 1]] = ids
+    return tokens, offsets, cluster, topics

@@ -11,6 +11,6 @@ from ._lib import (  # noqa: F401
     moe_combine, moe_dispatch, moe_expert_down, moe_expert_up, moe_grouped_gemm, moe_permute,
     moe_repack_ep_to_tp, moe_repack_tp_to_ep, moe_route, moe_route_permute, moe_route_workspace_bytes,
     moe_workspace_bytes, route_workspace, SwitchPolicy, switch_crossover, MODE_TP, MODE_EP,
-    SWITCH_STAY, SWITCH_TO_EP, SWITCH_TO_TP, SWITCH_VETOED,
+    SWITCH_STAY, SWITCH_TO_EP, SWITCH_TO_TP, SWITCH_VETOED, moe_schedule_requests, schedule_workspace,
 )
 from .layer import MoeLayerBuffers, moe_layer_forward  # noqa: F401

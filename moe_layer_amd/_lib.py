@@ -23,7 +23,8 @@ EXPORTED = (
     "moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes",
     "moe_route", "moe_route_permute", "moe_permute", "moe_grouped_gemm", "moe_expert_up",
     "moe_expert_down", "moe_combine", "moe_repack_ep_to_tp", "moe_repack_tp_to_ep", "moe_dispatch",
-    "moe_switch_init", "moe_switch_step", "moe_switch_crossover",
+    "moe_switch_init", "moe_switch_step", "moe_switch_crossover", "moe_schedule_workspace_bytes",
+    "moe_schedule_requests",
 )
 
 
@@ -97,6 +98,10 @@ def lib():
     L.moe_switch_step.argtypes = [ctypes.POINTER(SwitchState), ctypes.c_double, _i, ctypes.POINTER(_i)]
     L.moe_switch_crossover.restype = _i
     L.moe_switch_crossover.argtypes = [_dp, _dp, _dp, _i, _dp]
+    L.moe_schedule_workspace_bytes.restype = _sz
+    L.moe_schedule_workspace_bytes.argtypes = [_i, _i]
+    L.moe_schedule_requests.restype = _i
+    L.moe_schedule_requests.argtypes = [_p, _i, _p, _i, _p, _i, _i, _p, _p, _p, _p, _sz, _p]
     L.moe_dispatch.restype = _i
     L.moe_dispatch.argtypes = [_p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
     L.moe_repack_ep_to_tp.restype = _i
@@ -343,3 +348,24 @@ def switch_crossover(batches, t_tp, t_ep):
     _check("moe_switch_crossover", lib().moe_switch_crossover(arr(batches), arr(t_tp), arr(t_ep), n,
                                                               ctypes.byref(out)))
     return out.value
+
+
+def schedule_workspace(n_req, E, device="cuda"):
+    """A zero-filled workspace for moe_schedule_requests (left zero by every call)."""
+    n = max(lib().moe_schedule_workspace_bytes(n_req, E), 256)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_schedule_requests(tokens, req_offsets, cluster_of_token, E, scores, affinity, assigned, ws,
+                          stream=None):
+    """Attention-DP request scheduling: per-request cluster counts, the argmax
+    rank and the balanced rank (groups of E consecutive requests)."""
+    n_req = req_offsets.numel() - 1
+    st = lib().moe_schedule_requests(
+        _ptr(tokens, "tokens", torch.int32), tokens.numel(),
+        _ptr(req_offsets, "req_offsets", torch.int32), n_req,
+        _ptr(cluster_of_token, "cluster_of_token", torch.int32), cluster_of_token.numel(), E,
+        _ptr(scores, "scores", torch.int32, (n_req, E)), _ptr(affinity, "affinity", torch.int32, (n_req,)),
+        _ptr(assigned, "assigned", torch.int32, (n_req,)), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(stream))
+    _check("moe_schedule_requests", st)

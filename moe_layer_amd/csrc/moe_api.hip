@@ -25,7 +25,7 @@ using namespace moe;
 
 namespace {
 
-constexpr int ABI_VERSION = 6;
+constexpr int ABI_VERSION = 7;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -212,6 +212,27 @@ int moe_combine(const void* y_pair, const int32_t* pair_pos, const float* topk_w
   if (!aligned16(y_pair) || !aligned16(y) || !aligned4(pair_pos) || (topk_w && !aligned4(topk_w)))
     return MOE_EINVAL;
   launch_combine(dtype, y_pair, pair_pos, topk_w, T, kk, H, y, stream);
+  return launched();
+}
+
+size_t moe_schedule_workspace_bytes(int n_req, int E) { return schedule_workspace_bytes(n_req, E); }
+
+int moe_schedule_requests(const int32_t* tokens, int n_tokens, const int32_t* req_offsets, int n_req,
+                          const int32_t* cluster_of_token, int vocab, int E, int32_t* scores,
+                          int32_t* affinity, int32_t* assigned, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (n_tokens < 0 || n_req < 0 || vocab < 1 || E < 1) return MOE_EINVAL;
+  if (E > MAX_SCHED_RANKS || static_cast<long long>(n_req) * E > (1LL << 31) - 1) return MOE_EUNSUPPORTED;
+  if (n_tokens >= (1 << 25)) return MOE_EUNSUPPORTED;   // counts must stay below 2^25
+  if (n_req == 0) return MOE_OK;
+  if (!req_offsets || !cluster_of_token || !scores || !affinity || !assigned || (n_tokens > 0 && !tokens))
+    return MOE_EINVAL;
+  if (!aligned4(req_offsets) || !aligned4(cluster_of_token) || !aligned4(scores) || !aligned4(affinity) ||
+      !aligned4(assigned) || (tokens && !aligned4(tokens)))
+    return MOE_EINVAL;
+  if (!ws || !aligned4(ws) || ws_bytes < schedule_workspace_bytes(n_req, E)) return MOE_EWORKSPACE;
+  launch_schedule(tokens, n_tokens, req_offsets, n_req, cluster_of_token, vocab, E, scores, affinity,
+                  assigned, ws, stream);
   return launched();
 }
 

@@ -71,6 +71,14 @@ void launch_expert_down_tiles(const void* a, const int32_t* offsets, int n_group
 void launch_combine(int dtype, const void* y_pair, const int32_t* pair_pos, const float* w, int T,
                     int kk, int H, void* y, hipStream_t s);
 
+// Attention-DP request scheduling: per-request cluster counts, argmax rank,
+// and ranks balanced over groups of E consecutive requests (E <= 64).
+constexpr int MAX_SCHED_RANKS = 64;
+size_t schedule_workspace_bytes(int n_req, int E);
+void launch_schedule(const int32_t* tokens, int n_tokens, const int32_t* offsets, int n_req,
+                     const int32_t* cluster, int vocab, int E, int32_t* scores, int32_t* affinity,
+                     int32_t* assigned, void* ws, hipStream_t s);
+
 struct PeerPtrs {
   void* p[MAX_P];
 };

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_repack_ep_to_tp",
               "moe_repack_tp_to_ep", "moe_dispatch", "moe_switch_init", "moe_switch_step",
-              "moe_switch_crossover"):
+              "moe_switch_crossover", "moe_schedule_requests"):
         assert n in names
 
 
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 6
+    assert L.moe_abi_version() == 7
     for s in range(5):
         assert L.moe_status_str(s).decode().startswith(
             ["MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP"][s])
@@ -244,3 +244,23 @@ def test_repack_tp_to_ep_rejects(L):
     assert L.moe_repack_tp_to_ep(None, d, 2, 256, 128, 2, BF16, FAKE, FAKE, None) == MOE_EINVAL
     assert L.moe_repack_tp_to_ep(d, d, 2, 256, 128, 2, BF16, None, FAKE, None) == MOE_EINVAL
     assert L.moe_repack_tp_to_ep(d, d, 2, 256, 128, 2, BF16, FAKE, MISALIGNED, None) == MOE_EINVAL
+
+
+def test_schedule_rejects(L):
+    sch = lambda **kw: L.moe_schedule_requests(
+        kw.get("tok", FAKE), kw.get("nt", 100), kw.get("off", FAKE), kw.get("nr", 10), kw.get("cl", FAKE),
+        kw.get("V", 1000), kw.get("E", 8), kw.get("sc", FAKE), FAKE, FAKE, kw.get("ws", FAKE),
+        kw.get("wsb", 1 << 20), None)
+    assert sch(E=0) == MOE_EINVAL
+    assert sch(E=65) == MOE_EUNSUPPORTED
+    assert sch(nt=1 << 25) == MOE_EUNSUPPORTED
+    assert sch(V=0) == MOE_EINVAL
+    assert sch(nr=-1) == MOE_EINVAL
+    assert sch(nr=0) == MOE_OK                       # nothing to do, nothing launched
+    assert sch(off=None) == MOE_EINVAL
+    assert sch(tok=None) == MOE_EINVAL
+    assert sch(sc=MISALIGNED) == MOE_EINVAL
+    assert sch(ws=None) == MOE_EWORKSPACE
+    assert sch(wsb=4) == MOE_EWORKSPACE
+    assert L.moe_schedule_workspace_bytes(10, 8) == 256
+    assert L.moe_schedule_workspace_bytes(0, 8) == 0

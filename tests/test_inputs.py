@@ -98,3 +98,16 @@ def test_load_traces_are_seeded_and_shaped(kind):
         assert np.median(c) < 100 and c.max() > 400
     if kind == "rollout":
         assert c.max() >= 1000 and (c == 0).any()
+
+
+def test_requests_are_seeded_and_topical():
+    from moe_inputs.gen import make_requests
+    tok, off, cl, top = make_requests(200, 8, vocab=5000, seed=2)
+    tok2, off2, cl2, top2 = make_requests(200, 8, vocab=5000, seed=2)
+    assert np.array_equal(tok, tok2) and np.array_equal(off, off2) and np.array_equal(cl, cl2)
+    assert off[0] == 0 and (np.diff(off) >= 1).all() and off[-1] == tok.size
+    assert ((tok >= 0) & (tok < 5000)).all()
+    assert np.bincount(cl, minlength=8).tolist() == [625] * 8        # balanced clusters
+    # most of a request's tokens sit in its topic cluster
+    frac = [np.mean(cl[tok[off[r]:off[r + 1]]] == top[r]) for r in range(200)]
+    assert np.median(frac) > 0.5
