@@ -432,21 +432,28 @@ def algorithmic(wl):
 
 
 def time_workload(wl, steps, warmup, graph=False):
-    """K timed steps between two synchronisations.  Two HIP events per step,
-    recorded on the launch stream around the up-projection inside the same
-    timed region, give the dominant kernel's duration; a second pass with
-    events around every call gives the other kernels' durations."""
+    """K timed steps between two synchronisations, with nothing but the four
+    calls in the loop: an event record is a queue packet of its own and costs
+    the GPU ~5 us of idle time, so events would inflate the step.  A second
+    timed pass of K identical steps records two HIP events per step on the
+    launch stream around the up-projection: their mean is the dominant
+    kernel's duration.  A third pass with events around every call gives the
+    other kernels' durations (those include the event packets)."""
     import torch
     for i in range(warmup):
         run_step(wl, i)
-    up = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        run_step(wl, i, up_events=up[i])
+        run_step(wl, i)
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / steps
+    up = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        run_step(wl, i, up_events=up[i])
+    torch.cuda.synchronize()
     t_up_us = sum(a.elapsed_time(b) for a, b in up) / steps * 1e3
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
