@@ -236,15 +236,9 @@ __device__ __forceinline__ const char* tile_chunk(const WItem<NT>& it, int s, in
 // Weight bytes of one tile-chunk in the load layout: register i holds row
 // 4*(i%4) + l/16, bytes 256*(i/4) + 16*(l%16) of the chunk.  Non-temporal:
 // streamed once.  The loaded registers are not touched until use, so the
-// loads stay in flight.
-__device__ __forceinline__ void wload_full(const char* cbase, const uint32_t (&woff)[4],
-                                           uint4 (&w)[CHUNK_FRAGS]) {
-#pragma unroll
-  for (int i = 0; i < CHUNK_FRAGS; ++i) w[i] = ldg_nt(cbase + 256 * (i / 4), woff[i % 4]);
-}
-// The last chunk of K when it is partial (valid < 512 bytes): lanes past
-// the end re-read the chunk's first bytes of their row (finite data that
-// meets zero token fragments).
+// loads stay in flight.  When the chunk is the partial last one of K (valid
+// < 512 bytes), lanes past the end re-read the chunk's first bytes of their
+// row (finite data that meets zero token fragments).
 __device__ __forceinline__ void wload_part(const char* cbase, const uint32_t (&woff)[4], int valid,
                                            int lrow, uint4 (&w)[CHUNK_FRAGS]) {
 #pragma unroll
@@ -253,12 +247,13 @@ __device__ __forceinline__ void wload_part(const char* cbase, const uint32_t (&w
     w[i] = ldg_nt(cbase, woff[i % 4] + (col < valid ? 256 * (i / 4) : -16 * lrow));
   }
 }
+// One load sequence for full and partial chunks (the partial form gives the
+// full form's addresses when valid >= 512).  Loads behind a branch land in
+// different registers on the two paths; the join then copies registers and
+// the copies wait for the loads, draining the stream at every sub-step.
 __device__ __forceinline__ void wload(const char* cbase, const uint32_t (&woff)[4], int valid, int lrow,
                                       uint4 (&w)[CHUNK_FRAGS]) {
-  if (valid >= CHUNK_BYTES)
-    wload_full(cbase, woff, w);
-  else
-    wload_part(cbase, woff, valid, lrow, w);
+  wload_part(cbase, woff, valid, lrow, w);
 }
 
 // Token fragments of one chunk for every tile (cx = activations + chunk offset).
