@@ -37,8 +37,12 @@
 // covers every CU).  An item whose chunks fall into several waves' ranges is
 // split along K: each of those waves stores its fp32 partial tiles, and the
 // last of them to arrive (an integer counter per item; nobody waits) adds the
-// partials in K order and runs the epilogue.  The sum order depends only on
-// the shapes and the grid, so results are reproducible.  Waves are otherwise
+// partials in K order and runs the epilogue.  Only a range's first and last
+// items can be split; the first one's partial stays in registers and both are
+// handed over when the range's stream has ended, because the arrival count
+// must wait for the partial's stores, and in mid-stream that wait would also
+// wait for every weight load in flight.  The sum order depends only on the
+// shapes and the grid, so results are reproducible.  Waves are otherwise
 // independent: nothing synchronises them after start-up, so a slow load only
 // ever stalls its own wave.
 //
@@ -54,7 +58,15 @@
 // waits for the weights in flight.  All addresses are a wave-uniform base
 // plus a 32-bit lane offset (scalar-base loads, constant offsets folded into
 // the instructions).  The stream runs across item boundaries, and the next
-// item's token-row indices are fetched one item ahead.  Token rows past the
+// item's token-row indices are fetched one item ahead (at start-up, before
+// the first weight chunk, so forming them does not wait for it).
+//
+// Every load sits on the straight-line path: the next chunk's base is chosen
+// with scalar selects, and K that is a whole number of 512-byte chunks gets
+// its own instantiation without the partial-chunk masks.  A load issued on
+// one side of a branch lands in other registers than on the other side; the
+// join then copies them, and the copy waits for the load -- and, loads
+// retiring in order, for all the weight loads issued before it.  Token rows past the
 // group's count repeat a real row and are never stored; fragments past the
 // end of K are zero on both sides.  Every output element is written by
 // exactly one lane.
@@ -62,6 +74,7 @@
 #include "moe_internal.h"
 
 namespace moe {
+
 
 constexpr int XW_WAVES = 4;                             // waves per block (independent)
 constexpr int CHUNK_FRAGS = 8;                          // 64-byte fragments per chunk
@@ -218,6 +231,24 @@ __device__ __forceinline__ void witem_tokens(const XArgs& a, int lrow, int lq, u
     it.xoff[tt] = static_cast<uint32_t>(tok) * row_bytes + 16 * lq;
   }
 }
+// The same in two steps: fetch the rows' pair ids, then form the offsets.
+template <typename T, int MODE, int NT>
+__device__ __forceinline__ void witem_token_ids(const XArgs& a, int lrow, const WItem<NT>& it, int (&raw)[NT]) {
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int r = it.row0 + min(it.t0 + tt * 16 + lrow, it.m_end - 1);
+    raw[tt] = (MODE == XMODE_UP) ? a.sorted_pair[r] : r;
+  }
+}
+template <typename T, int MODE, int NT>
+__device__ __forceinline__ void witem_token_offsets(const XArgs& a, int lq, uint32_t row_bytes, const int (&raw)[NT],
+                                                    WItem<NT>& it) {
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int tok = (MODE == XMODE_UP) ? raw[tt] / a.kk : raw[tt];
+    it.xoff[tt] = static_cast<uint32_t>(tok) * row_bytes + 16 * lq;
+  }
+}
 
 template <typename T, int MODE, int NT, int SUB>
 __device__ __forceinline__ void witem_setup(const XArgs& a, const int* s_istart, const int* s_off,
@@ -246,6 +277,10 @@ __device__ __forceinline__ void wload_part(const char* cbase, const uint32_t (&w
     const int col = 256 * (i / 4) + 16 * lrow;
     w[i] = ldg_nt(cbase, woff[i % 4] + (col < valid ? 256 * (i / 4) : -16 * lrow));
   }
+}
+__device__ __forceinline__ void wload_full(const char* cbase, const uint32_t (&woff)[4], uint4 (&w)[CHUNK_FRAGS]) {
+#pragma unroll
+  for (int i = 0; i < CHUNK_FRAGS; ++i) w[i] = ldg_nt(cbase + 256 * (i / 4), woff[i % 4]);
 }
 // One load sequence for full and partial chunks (the partial form gives the
 // full form's addresses when valid >= 512).  Loads behind a branch land in
@@ -364,16 +399,11 @@ __device__ __forceinline__ float* part_slot(const XArgs& a, int tiles, int w, in
   return a.part + (static_cast<size_t>(w) * 2 + which) * tiles * WAVE * 4;
 }
 
-// The item's chunks were split over waves wa..wb (K order).  Store this
-// wave's partial; the last wave to arrive sums all of them in K order and
-// runs the epilogue.
+// Store this wave's partial of a split item (agent scope, no wait).
 template <typename T, int MODE, int NT, int SUB>
-__device__ __forceinline__ void finish_split(const XArgs& a, const WItem<NT>& it, f32x4_t (&acc)[SUB][NT],
-                                             int item, int w, int W, long long Q, int lrow, int lq) {
+__device__ __forceinline__ void split_publish(const XArgs& a, const f32x4_t (&acc)[SUB][NT], int item, int w, int W,
+                                              long long Q) {
   const int l = lane_id();
-  const long long qa = static_cast<long long>(item) * a.nck;
-  const int wa = chunk_owner(qa, Q, W);
-  const int wb = chunk_owner(qa + a.nck - 1, Q, W);
   uint64_t* mine = reinterpret_cast<uint64_t*>(part_slot(a, SUB * NT, w, item, Q, W));
 #pragma unroll
   for (int s = 0; s < SUB; ++s)
@@ -383,11 +413,23 @@ __device__ __forceinline__ void finish_split(const XArgs& a, const WItem<NT>& it
       st_agent(p, (static_cast<uint64_t>(__float_as_uint(acc[s][tt][1])) << 32) | __float_as_uint(acc[s][tt][0]));
       st_agent(p + 1, (static_cast<uint64_t>(__float_as_uint(acc[s][tt][3])) << 32) | __float_as_uint(acc[s][tt][2]));
     }
-  __builtin_amdgcn_s_waitcnt(0);  // the partial is performed (agent scope) before the count
-  int old = 0;
-  if (l == 0) old = atomicAdd(a.ctr + item, 1);
-  old = __shfl(old, 0, WAVE);
-  if (old == wb - wa) {  // last to arrive (wave-uniform)
+}
+
+// Arrivals counted for a split item so far, before this one, equals the
+// number of other contributors: this wave is the last.
+__device__ __forceinline__ int split_others(const XArgs& a, int item, long long Q, int W) {
+  const long long qa = static_cast<long long>(item) * a.nck;
+  return chunk_owner(qa + a.nck - 1, Q, W) - chunk_owner(qa, Q, W);
+}
+
+template <typename T, int MODE, int NT, int SUB>
+__device__ __forceinline__ void split_reduce(const XArgs& a, const WItem<NT>& it, f32x4_t (&acc)[SUB][NT],
+                                             int item, int w, int W, long long Q, int lrow, int lq, bool last) {
+  const int l = lane_id();
+  const long long qa = static_cast<long long>(item) * a.nck;
+  const int wa = chunk_owner(qa, Q, W);
+  const int wb = chunk_owner(qa + a.nck - 1, Q, W);
+  if (last) {  // last to arrive (wave-uniform)
     if (l == 0) st_agent(a.ctr + item, 0);
     f32x4_t sum[SUB][NT];
     for (int v = wa; v <= wb; ++v) {
@@ -419,7 +461,7 @@ __device__ __forceinline__ void finish_split(const XArgs& a, const WItem<NT>& it
     for (int tt = 0; tt < NT; ++tt) acc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-template <typename T, int MODE, int NT, int SUB>
+template <typename T, int MODE, int NT, int SUB, bool FULLK>
 __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   __shared__ int s_istart[MAX_GROUPS + 1];
   __shared__ int s_off[MAX_GROUPS + 1];
@@ -451,12 +493,26 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   // The first weight chunk goes out before the token indices are fetched.
   WItem<NT> cur, nxt;
   witem_weights<T, MODE, NT, SUB>(a, s_istart, s_off, item, lrow, lq, row_bytes, cur);
+  nxt = cur;
   uint4 w0[CHUNK_FRAGS], w1[CHUNK_FRAGS], x[NT][CHUNK_FRAGS];
   int c = cb;
-  wload(tile_chunk(cur, 0, c), cur.woff, kbytes - c * CHUNK_BYTES, lrow, w0);
-  witem_tokens<T, MODE, NT>(a, lrow, lq, row_bytes, cur);
+  // Token ids first, then the first weight chunk: forming the token offsets
+  // then waits only for the ids, not for the weight chunk behind them.
+  int raw_c[NT], raw_n[NT];
+  witem_token_ids<T, MODE, NT>(a, lrow, cur, raw_c);
   bool have_nxt = static_cast<long long>(item + 1) * a.nck < q1;
-  if (have_nxt) witem_setup<T, MODE, NT, SUB>(a, s_istart, s_off, item + 1, lrow, lq, row_bytes, nxt);
+  if (have_nxt) {
+    witem_weights<T, MODE, NT, SUB>(a, s_istart, s_off, item + 1, lrow, lq, row_bytes, nxt);
+    witem_token_ids<T, MODE, NT>(a, lrow, nxt, raw_n);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (FULLK)
+    wload_full(tile_chunk(cur, 0, c), cur.woff, w0);
+  else
+    wload(tile_chunk(cur, 0, c), cur.woff, kbytes - c * CHUNK_BYTES, lrow, w0);
+  __builtin_amdgcn_sched_barrier(0);
+  witem_token_offsets<T, MODE, NT>(a, lq, row_bytes, raw_c, cur);
+  if (have_nxt) witem_token_offsets<T, MODE, NT>(a, lq, row_bytes, raw_n, nxt);
 
   f32x4_t acc[SUB][NT];
 #pragma unroll
@@ -474,19 +530,28 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   // path.
 #define XSUB(S, WC, WN)                                                                   \
   if constexpr (S < SUB) {                                                                \
-    if (S + 1 < SUB) {                                                                    \
-      wload(tile_chunk(cur, S + 1, c), cur.woff, cvalid, lrow, WN);                       \
-    } else if (!last) {                                                                   \
-      wload(tile_chunk(cur, 0, c + 1), cur.woff, cvalid - CHUNK_BYTES, lrow, WN);         \
-    } else if (have_nxt) {                                                                \
-      wload(tile_chunk(nxt, 0, 0), nxt.woff, kbytes, lrow, WN);                           \
-    } else {                                                                              \
-      wload(tile_chunk(cur, 0, c), cur.woff, cvalid, lrow, WN);                           \
+    {                                                                                     \
+      const char* nb;                                                                     \
+      int nv;                                                                             \
+      if (S + 1 < SUB) {                                                                  \
+        nb = tile_chunk(cur, S + 1, c);                                                   \
+        nv = cvalid;                                                                      \
+      } else {                                                                            \
+        const char* b_next = tile_chunk(cur, 0, c + 1);                                   \
+        const char* b_item = tile_chunk(nxt, 0, 0);                                       \
+        const char* b_same = tile_chunk(cur, 0, c);                                       \
+        nb = !last ? b_next : (have_nxt ? b_item : b_same);                               \
+        nv = !last ? cvalid - CHUNK_BYTES : (have_nxt ? kbytes : cvalid);                 \
+      }                                                                                   \
+      if constexpr (FULLK)                                                                \
+        wload_full(nb, cur.woff, WN);                                                     \
+      else                                                                                \
+        wload(nb, cur.woff, nv, lrow, WN);                                                \
     }                                                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     uint4 wt[CHUNK_FRAGS];                                                                \
     wtranspose(WC, tile, lrow, lq, wt);                                                   \
-    if (cvalid >= CHUNK_BYTES)                                                            \
+    if (FULLK || cvalid >= CHUNK_BYTES)                                                   \
       wmma_full<T, NT>(wt, x, acc[S]);                                                    \
     else                                                                                  \
       wmma_part<T, NT>(wt, x, cvalid / FRAG_BYTES, acc[S]);                               \
@@ -499,7 +564,7 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
 #define CSTEP(WA, WB)                                                                     \
   {                                                                                       \
     const int cvalid = kbytes - c * CHUNK_BYTES; /* bytes of K left from this chunk on */ \
-    if (cvalid >= CHUNK_BYTES)                                                            \
+    if constexpr (FULLK)                                                                  \
       xload_full<NT>(act + c * CHUNK_BYTES, cur.xoff, x);                                 \
     else                                                                                  \
       xload_part<NT>(act + c * CHUNK_BYTES, cur.xoff, cvalid / FRAG_BYTES, x);            \
@@ -512,10 +577,13 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
     if (!last) {                                                                          \
       ++c;                                                                                \
     } else {                                                                              \
-      if (cb == 0 && ce == a.nck)                                                         \
+      if (cb == 0 && ce == a.nck) {                                                       \
         wstore<T, MODE, NT, SUB>(a, cur, acc, lrow, lq);                                  \
-      else                                                                                \
-        finish_split<T, MODE, NT, SUB>(a, cur, acc, item, w, W, Q, lrow, lq);             \
+      } else if (have_nxt) {                                                              \
+        HOLD_STORE                                                                        \
+      } else {                                                                            \
+        break;                                                                            \
+      }                                                                                   \
       if (!have_nxt) break;                                                               \
       ++item;                                                                             \
       cur = nxt;                                                                          \
@@ -528,6 +596,19 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
     }                                                                                     \
   }
 
+  f32x4_t hold[SUB][NT];
+  WItem<NT> hold_it = cur;
+  int hold_item = -1;
+#define HOLD_STORE                                                                        \
+  {                                                                                       \
+    _Pragma("unroll") for (int s_ = 0; s_ < SUB; ++s_)                                    \
+      _Pragma("unroll") for (int t_ = 0; t_ < NT; ++t_) {                                 \
+        hold[s_][t_] = acc[s_][t_];                                                       \
+        acc[s_][t_] = f32x4_t{0.f, 0.f, 0.f, 0.f};                                        \
+      }                                                                                   \
+    hold_it = cur;                                                                        \
+    hold_item = item;                                                                     \
+  }
   static_assert(SUB == 1 || SUB == 2 || SUB == 4, "tiles per item");
   if constexpr (SUB % 2 == 0) {
     while (true) CSTEP(w0, w1)
@@ -539,6 +620,24 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   }
 #undef CSTEP
 #undef XSUB
+#undef HOLD_STORE
+  {
+    // Both split items of the range at once: partials, one wait, both counts.
+    const bool h_ = hold_item >= 0;
+    const bool e_ = !(cb == 0 && ce == a.nck);
+    if (h_) split_publish<T, MODE, NT, SUB>(a, hold, hold_item, w, W, Q);
+    if (e_) split_publish<T, MODE, NT, SUB>(a, acc, item, w, W, Q);
+    __builtin_amdgcn_s_waitcnt(0);  // the partials are performed (agent scope) before the counts
+    int o1 = 0, o2 = 0;
+    if (lane_id() == 0) {
+      if (h_) o1 = atomicAdd(a.ctr + hold_item, 1);
+      if (e_) o2 = atomicAdd(a.ctr + item, 1);
+    }
+    o1 = __shfl(o1, 0, WAVE);
+    o2 = __shfl(o2, 0, WAVE);
+    if (h_) split_reduce<T, MODE, NT, SUB>(a, hold_it, hold, hold_item, w, W, Q, lrow, lq, o1 == split_others(a, hold_item, Q, W));
+    if (e_) split_reduce<T, MODE, NT, SUB>(a, cur, acc, item, w, W, Q, lrow, lq, o2 == split_others(a, item, Q, W));
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -632,28 +731,39 @@ size_t expert_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dty
   return stream_workspace_bytes(T, kk, n_groups, H, I, dtype) + expert_tile_workspace_bytes(T, kk, n_groups, H, I, dtype);
 }
 
-template <typename T, int MODE, int NT, int SUB>
+template <typename T, int MODE, int NT, int SUB, bool FULLK>
 static int resident_blocks() {
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&expert_wave_kernel<T, MODE, NT, SUB>), XW_WAVES * WAVE, 0) !=
+            &n, reinterpret_cast<const void*>(&expert_wave_kernel<T, MODE, NT, SUB, FULLK>), XW_WAVES * WAVE, 0) !=
             hipSuccess || n < 1)
       n = 1;
-    per_cu = n;
+    // The streaming rate drops with more than two blocks of four waves per
+    // CU (more concurrent row streams); kernels with two token tiles fit one.
+    per_cu = n < 2 ? n : 2;
   }
   long long g = static_cast<long long>(device_cu_count()) * per_cu;
   if (g * XW_WAVES > MAX_WAVES) g = MAX_WAVES / XW_WAVES;
   return static_cast<int>(g);
 }
 
-template <typename T, int MODE, int NT, int SUB>
-static void launch_t(XArgs a, hipStream_t s) {
-  const int grid = resident_blocks<T, MODE, NT, SUB>();
+template <typename T, int MODE, int NT, int SUB, bool FULLK>
+static void launch_k(XArgs a, hipStream_t s) {
+  const int grid = resident_blocks<T, MODE, NT, SUB, FULLK>();
   a.waves = grid * XW_WAVES;
   a.n_quads = (a.n_tiles + SUB - 1) / SUB;
-  hipLaunchKernelGGL((expert_wave_kernel<T, MODE, NT, SUB>), dim3(grid), dim3(XW_WAVES * WAVE), 0, s, a);
+  hipLaunchKernelGGL((expert_wave_kernel<T, MODE, NT, SUB, FULLK>), dim3(grid), dim3(XW_WAVES * WAVE), 0, s, a);
+}
+
+// K a whole number of 512-byte chunks: no partial chunk, no masking.
+template <typename T, int MODE, int NT, int SUB>
+static void launch_t(XArgs a, hipStream_t s) {
+  if (a.kfrag_total % CHUNK_FRAGS == 0)
+    launch_k<T, MODE, NT, SUB, true>(a, s);
+  else
+    launch_k<T, MODE, NT, SUB, false>(a, s);
 }
 
 template <typename T, int MODE>
