@@ -13,8 +13,8 @@
 // decision from the same counts and skips exactly those groups.
 //
 // Work item = (group g, SUB adjacent weight tiles (1 or 4, per launch), pass
-// of 16 token rows -- 32 in the two-tile kernel when the group has more than
-// 16) over the full K.  A weight tile is 16 rows:
+// of 16 token rows -- 16*NT in the kernels holding NT = 2 or 4 token tiles
+// when the group has more than 16) over the full K.  A weight tile is 16 rows:
 //   up   : 8 gate rows and the matching 8 up rows, so SiLU(gate)*up is
 //          formed in registers;
 //   down : 16 rows of W2 = 16 output features.
@@ -81,8 +81,8 @@ constexpr int CHUNK_FRAGS = 8;                          // 64-byte fragments per
 constexpr int CHUNK_BYTES = CHUNK_FRAGS * FRAG_BYTES;   // 512
 constexpr int SUB_MAX = 4;                              // weight tiles per item at most
 constexpr int MIN_CPW = 2;                              // chunks per wave at least (bounds split items)
-constexpr int MAX_WAVES = 4096;                         // waves of one launch at most
-constexpr int NT_MAX = 2;
+constexpr int MAX_WAVES = 2048;                         // waves of one launch at most
+constexpr int NT_MAX = 4;
 
 enum XMode { XMODE_UP = 0, XMODE_DOWN = 1 };
 
@@ -103,37 +103,57 @@ struct XArgs {
   int nck;                 // 512-byte chunks per item
   int waves;               // waves launched
   int tile_nt;             // > 0: the tile kernel ran first with this many weight tiles per group ...
-  int tile_min;            // ... and took the groups above TILE_M_MIN rows if they made this many tiles
+  int tile_min;            // ... and took the groups above tile_m_min rows if they made this many tiles
+  int tile_m_min;
   int* ctr;                // per-item arrival counters (zero between calls)
   float* part;             // per-wave partial tiles: [wave][2][SUB][NT][64 lanes][4]
 };
 
-// Token rows per pass of a group with m rows: 16, or 32 when the kernel
-// holds two token tiles and the group has more than 16 rows.
+// Token rows per pass of a group with m rows: 16, or 16*NT when the kernel
+// holds NT token tiles and the group has more than 16 rows.
 template <int NT>
 __device__ __forceinline__ int pass_rows(int m) {
-  return (NT == 2 && m > 16) ? 32 : 16;
+  return (NT > 1 && m > 16) ? 16 * NT : 16;
 }
 
 // Wave 0: s_off[g] = offsets[g]; s_istart[g] = items of the groups before g
-// (passes x quads each); s_istart[n_groups] = total items.
+// (passes x quads each); s_istart[n_groups] = total items; *s_ntx = token
+// tiles of the pass (a kernel built for four runs two when every group it
+// takes holds 32 rows or fewer: four cost more per chunk than they save).
 template <int NT>
 __device__ __forceinline__ void item_prefix(const int* __restrict__ offsets, int n_groups, int n_quads,
-                                            int tile_nt, int tile_min, int* s_istart, int* s_off) {
+                                            int tile_nt, int tile_min, int tile_m_min, int* s_istart, int* s_off,
+                                            int* s_ntx) {
   if (threadIdx.x >= WAVE) return;
   const int l = lane_id();
-  // The tile kernel's decision, by the same formula: it took the groups with
-  // more than TILE_M_MIN rows if they make at least tile_min tiles.
+  // The tile kernel's decision, by the same formula: it runs if the groups
+  // with more than TILE_M_MIN rows make at least tile_min tiles, and takes
+  // the groups above tile_m_min rows when there are none (every group then
+  // fits one pass here), else all groups above TILE_M_MIN.
   int m_max = 0x7fffffff;
   if (tile_nt > 0) {
-    int tiles = 0;
+    int t32 = 0, twide = 0;
     for (int g = l; g < n_groups; g += WAVE) {
       const int m = offsets[g + 1] - offsets[g];
-      if (m > TILE_M_MIN) tiles += (m + TILE_ROWS - 1) / TILE_ROWS * tile_nt;
+      const int t = (m + TILE_ROWS - 1) / TILE_ROWS * tile_nt;
+      if (m > TILE_M_MIN) t32 += t;
+      if (m > tile_m_min) twide += t;
     }
 #pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) tiles += __shfl_xor(tiles, d, WAVE);
-    if (tiles >= tile_min) m_max = TILE_M_MIN;
+    for (int d = 1; d < WAVE; d <<= 1) {
+      t32 += __shfl_xor(t32, d, WAVE);
+      twide += __shfl_xor(twide, d, WAVE);
+    }
+    if (t32 >= tile_min) m_max = twide == 0 ? tile_m_min : TILE_M_MIN;
+  }
+  int ntx = NT;
+  if (NT == 4) {
+    int big = 0;
+    for (int g = l; g < n_groups; g += WAVE) {
+      const int m = offsets[g + 1] - offsets[g];
+      big |= (m > 32 && m <= m_max) ? 1 : 0;
+    }
+    ntx = __any(big) ? 4 : 2;
   }
   int base = 0;
   for (int g0 = 0; g0 <= n_groups; g0 += WAVE) {
@@ -142,14 +162,17 @@ __device__ __forceinline__ void item_prefix(const int* __restrict__ offsets, int
     int v = 0;
     if (g < n_groups) {
       const int m = offsets[g + 1] - offsets[g];
-      const int ps = pass_rows<NT>(m);
+      const int ps = (ntx > 1 && m > 16) ? 16 * ntx : 16;  // pass_rows of the kernel body that runs
       if (m <= m_max) v = (m + ps - 1) / ps * n_quads;
     }
     const int incl = wave_inclusive_scan(v);
     if (g < n_groups) s_istart[g] = base + incl - v;
     base += __shfl(incl, WAVE - 1, WAVE);
   }
-  if (l == 0) s_istart[n_groups] = base;
+  if (l == 0) {
+    s_istart[n_groups] = base;
+    *s_ntx = ntx;
+  }
 }
 
 // Loads from a wave-uniform base (kept in SGPRs) plus a 32-bit lane offset:
@@ -293,22 +316,26 @@ __device__ __forceinline__ void wload(const char* cbase, const uint32_t (&woff)[
 
 // Token fragments of one chunk for every tile (cx = activations + chunk offset).
 template <int NT>
-__device__ __forceinline__ void xload_full(const char* cx, const uint32_t (&xoff)[NT],
+__device__ __forceinline__ void xload_full(const char* cx, const uint32_t (&xoff)[NT], int nrows,
                                            uint4 (&x)[NT][CHUNK_FRAGS]) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt)
+    if (tt == 0 || 16 * tt < nrows) {
 #pragma unroll
-    for (int f = 0; f < CHUNK_FRAGS; ++f) x[tt][f] = ldg(cx + FRAG_BYTES * f, xoff[tt]);
+      for (int f = 0; f < CHUNK_FRAGS; ++f) x[tt][f] = ldg(cx + FRAG_BYTES * f, xoff[tt]);
+    }
 }
 // Partial chunk: fragments past the end of K re-read a valid one; wmma_part
 // zeroes them at use.
 template <int NT>
-__device__ __forceinline__ void xload_part(const char* cx, const uint32_t (&xoff)[NT], int nf,
+__device__ __forceinline__ void xload_part(const char* cx, const uint32_t (&xoff)[NT], int nf, int nrows,
                                            uint4 (&x)[NT][CHUNK_FRAGS]) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt)
+    if (tt == 0 || 16 * tt < nrows) {
 #pragma unroll
-    for (int f = 0; f < CHUNK_FRAGS; ++f) x[tt][f] = ldg(cx, xoff[tt] + FRAG_BYTES * min(f, nf - 1));
+      for (int f = 0; f < CHUNK_FRAGS; ++f) x[tt][f] = ldg(cx, xoff[tt] + FRAG_BYTES * min(f, nf - 1));
+    }
 }
 
 constexpr int WT_ROW = CHUNK_BYTES + 16;  // padded row of the wave's LDS tile
@@ -325,25 +352,32 @@ __device__ __forceinline__ void wtranspose(const uint4 (&w)[CHUNK_FRAGS], char* 
     wt[f] = *reinterpret_cast<const uint4*>(tile + lrow * WT_ROW + FRAG_BYTES * f + 16 * lq);
 }
 
-// A token tile past the pass's rows (repeated rows) is multiplied too --
-// branching around it costs more than the MFMAs -- and never stored.
+// Token tiles wholly past the pass's rows (nrows of them hold real rows) are
+// skipped: a uniform branch around MFMAs only, no loads.  Rows past the end
+// inside a tile repeat a real row and are never stored.
 template <typename T, int NT>
 __device__ __forceinline__ void wmma_full(const uint4 (&w)[CHUNK_FRAGS], const uint4 (&x)[NT][CHUNK_FRAGS],
-                                          f32x4_t (&acc)[NT]) {
+                                          int nrows, f32x4_t (&acc)[NT]) {
 #pragma unroll
-  for (int f = 0; f < CHUNK_FRAGS; ++f)
+  for (int tt = 0; tt < NT; ++tt) {
+    if (tt == 0 || 16 * tt < nrows) {
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) acc[tt] = Elem<T>::mma(w[f], x[tt][f], acc[tt]);
+      for (int f = 0; f < CHUNK_FRAGS; ++f) acc[tt] = Elem<T>::mma(w[f], x[tt][f], acc[tt]);
+    }
+  }
 }
 // Fragments f >= nf lie past the end of K: their token side is zeroed here,
 // so they add exactly nothing whatever the weight side holds.
 template <typename T, int NT>
 __device__ __forceinline__ void wmma_part(const uint4 (&w)[CHUNK_FRAGS], const uint4 (&x)[NT][CHUNK_FRAGS],
-                                          int nf, f32x4_t (&acc)[NT]) {
+                                          int nf, int nrows, f32x4_t (&acc)[NT]) {
 #pragma unroll
-  for (int f = 0; f < CHUNK_FRAGS; ++f)
+  for (int tt = 0; tt < NT; ++tt) {
+    if (tt == 0 || 16 * tt < nrows) {
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) acc[tt] = Elem<T>::mma(w[f], keep_or_zero(f < nf, x[tt][f]), acc[tt]);
+      for (int f = 0; f < CHUNK_FRAGS; ++f) acc[tt] = Elem<T>::mma(w[f], keep_or_zero(f < nf, x[tt][f]), acc[tt]);
+    }
+  }
 }
 
 // acc[s][tt][r] = D[4*lq + r][lrow] of tile s: weight row 4*lq+r of the
@@ -461,19 +495,10 @@ __device__ __forceinline__ void split_reduce(const XArgs& a, const WItem<NT>& it
     for (int tt = 0; tt < NT; ++tt) acc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
+// The streaming part of the kernel, after the item table is built.
 template <typename T, int MODE, int NT, int SUB, bool FULLK>
-__global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
-  __shared__ int s_istart[MAX_GROUPS + 1];
-  __shared__ int s_off[MAX_GROUPS + 1];
-  __shared__ __attribute__((aligned(16))) char s_wt[XW_WAVES][16 * WT_ROW];
-
-  const int wv = uni(threadIdx.x / WAVE);
-  const int l = lane_id();
-  const int lrow = l & 15;
-  const int lq = l >> 4;
-
-  item_prefix<NT>(a.offsets, a.n_groups, a.n_quads, a.tile_nt, a.tile_min, s_istart, s_off);
-  __syncthreads();  // the only barrier; waves are independent from here on
+__device__ __forceinline__ void stream_body(const XArgs& a, const int* s_istart, const int* s_off, char* tile,
+                                            int wv, int l, int lrow, int lq) {
   const long long Q = static_cast<long long>(uni(s_istart[a.n_groups])) * a.nck;
   const int W = static_cast<int>(min(static_cast<long long>(a.waves), (Q + MIN_CPW - 1) / MIN_CPW));
   const int w = wv * gridDim.x + blockIdx.x;
@@ -519,7 +544,6 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   for (int s = 0; s < SUB; ++s)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  char* tile = s_wt[wv];
 
   // Sub-step S of a chunk step: load the next tile-chunk into WN (tile S+1
   // of this chunk; after the last tile, tile 0 of the next chunk, of the next
@@ -552,9 +576,9 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
     uint4 wt[CHUNK_FRAGS];                                                                \
     wtranspose(WC, tile, lrow, lq, wt);                                                   \
     if (FULLK || cvalid >= CHUNK_BYTES)                                                   \
-      wmma_full<T, NT>(wt, x, acc[S]);                                                    \
+      wmma_full<T, NT>(wt, x, cur.m_end - cur.t0, acc[S]);                                \
     else                                                                                  \
-      wmma_part<T, NT>(wt, x, cvalid / FRAG_BYTES, acc[S]);                               \
+      wmma_part<T, NT>(wt, x, cvalid / FRAG_BYTES, cur.m_end - cur.t0, acc[S]);           \
   }
 
   // One chunk step: the chunk's token fragments, then the SUB tiles (the
@@ -565,9 +589,9 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   {                                                                                       \
     const int cvalid = kbytes - c * CHUNK_BYTES; /* bytes of K left from this chunk on */ \
     if constexpr (FULLK)                                                                  \
-      xload_full<NT>(act + c * CHUNK_BYTES, cur.xoff, x);                                 \
+      xload_full<NT>(act + c * CHUNK_BYTES, cur.xoff, cur.m_end - cur.t0, x);             \
     else                                                                                  \
-      xload_part<NT>(act + c * CHUNK_BYTES, cur.xoff, cvalid / FRAG_BYTES, x);            \
+      xload_part<NT>(act + c * CHUNK_BYTES, cur.xoff, cvalid / FRAG_BYTES, cur.m_end - cur.t0, x); \
     __builtin_amdgcn_sched_barrier(0); /* token loads stay ahead of the weight loads */   \
     const bool last = c + 1 >= ce;                                                        \
     XSUB(0, WA, WB)                                                                       \
@@ -640,16 +664,49 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   }
 }
 
+template <typename T, int MODE, int NT, int SUB, bool FULLK>
+__global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
+  __shared__ int s_istart[MAX_GROUPS + 1];
+  __shared__ int s_off[MAX_GROUPS + 1];
+  __shared__ int s_ntx;
+  __shared__ __attribute__((aligned(16))) char s_wt[XW_WAVES][16 * WT_ROW];
+
+  const int wv = uni(threadIdx.x / WAVE);
+  const int l = lane_id();
+  const int lrow = l & 15;
+  const int lq = l >> 4;
+
+  item_prefix<NT>(a.offsets, a.n_groups, a.n_quads, a.tile_nt, a.tile_min, a.tile_m_min, s_istart, s_off, &s_ntx);
+  __syncthreads();  // the only barrier; waves are independent from here on
+  if constexpr (NT == 4) {
+    if (uni(s_ntx) == 4)
+      stream_body<T, MODE, 4, SUB, FULLK>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
+    else
+      stream_body<T, MODE, 2, SUB, FULLK>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
+  } else {
+    stream_body<T, MODE, NT, SUB, FULLK>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 static int elem_bytes_x(int dtype) { return dtype == 1 ? 2 : 4; }
 
-// Two token tiles from the mean rows per group (exact for the full and TP
-// views; an over-estimate for an EP share).  In that kernel a group with at
-// most 16 rows still runs one 16-row pass.
+// Token tiles from the mean rows per group (exact for the full and TP views;
+// an over-estimate for an EP share): two above 12; four for batches of
+// 384..767 tokens with more than 24 (groups of 33..64 rows then take one pass
+// instead of two, or the LDS-tiled kernel, which is latency-bound with few
+// tiles).  Four tiles need one wave per SIMD and compute more per chunk, so
+// they lose wherever groups hold 32 rows or fewer.
 static int pick_nt(int T, int kk, int n_groups) {
   const double mean = static_cast<double>(T) * kk / n_groups;
-  return (mean > 12.0 && T > 16) ? 2 : 1;
+  if (T <= 16) return 1;
+  if (T >= 384 && T < 768 && mean > 24.0) return 4;
+  return mean > 12.0 ? 2 : 1;
+}
+
+int expert_tile_m_min(int T, int kk, int n_groups) {
+  return pick_nt(T, kk, n_groups) == 4 ? TILE_M_MIN_WIDE : TILE_M_MIN;
 }
 
 struct XShape {
@@ -670,7 +727,7 @@ static XShape x_shape(int mode, int H, int I, int dtype) {
 // (under 16 KB); else one.
 static int pick_sub(int nt, int kfrag_total) {
   const long long tile_bytes = 16LL * kfrag_total * FRAG_BYTES;
-  return (nt == 2 || tile_bytes < 16384) ? 4 : 1;
+  return (nt >= 2 || tile_bytes < 16384) ? 4 : 1;
 }
 
 // Items of one launch at most: sum over groups of ceil(m_g / 16) passes
@@ -768,7 +825,8 @@ static void launch_t(XArgs a, hipStream_t s) {
 
 template <typename T, int MODE>
 static void launch_tm(XArgs a, int nt, int sub, hipStream_t s) {
-  if (nt == 2) launch_t<T, MODE, 2, 4>(a, s);
+  if (nt == 4) launch_t<T, MODE, 4, 4>(a, s);
+  else if (nt == 2) launch_t<T, MODE, 2, 4>(a, s);
   else if (sub == 4) launch_t<T, MODE, 1, 4>(a, s);
   else launch_t<T, MODE, 1, 1>(a, s);
 }
@@ -777,6 +835,7 @@ template <int MODE>
 static void launch_mode(int dtype, XArgs a, int T, int kk, void* ws, hipStream_t s) {
   a.tile_nt = expert_tile_used(T, dtype) ? expert_tile_nt(MODE == XMODE_UP, a.H, a.I_loc) : 0;
   a.tile_min = expert_tile_min_tiles();
+  a.tile_m_min = expert_tile_m_min(T, kk, a.n_groups);
   const XShape sh = x_shape(MODE, a.H, a.I_loc, dtype);
   a.n_tiles = sh.n_tiles;
   a.kfrag_total = sh.kfrag_total;
@@ -807,7 +866,7 @@ void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, cons
   a.I_loc = I;
   a.H = H;
   if (expert_tile_used(T, dtype))
-    launch_expert_up_tiles(x, sorted_pair, offsets, n_groups, T, kk, w13, H, I, A,
+    launch_expert_up_tiles(x, sorted_pair, offsets, n_groups, T, kk, w13, H, I, A, expert_tile_m_min(T, kk, n_groups),
                            static_cast<char*>(ws) + stream_workspace_bytes(T, kk, n_groups, H, I, dtype), s);
   launch_mode<XMODE_UP>(dtype, a, T, kk, ws, s);
 }
@@ -825,7 +884,7 @@ void launch_expert_down(int dtype, const void* A, const int32_t* offsets, int n_
   a.I_loc = I;
   a.H = H;
   if (expert_tile_used(T, dtype))
-    launch_expert_down_tiles(A, offsets, n_groups, T, kk, w2, H, I, y_pair,
+    launch_expert_down_tiles(A, offsets, n_groups, T, kk, w2, H, I, y_pair, expert_tile_m_min(T, kk, n_groups),
                              static_cast<char*>(ws) + stream_workspace_bytes(T, kk, n_groups, H, I, dtype), s);
   launch_mode<XMODE_DOWN>(dtype, a, T, kk, ws, s);
 }

@@ -101,9 +101,26 @@ __device__ __forceinline__ int tl_wrow(int tid) {
 __device__ __forceinline__ int tl_uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Wave 0: s_off[g] = offsets[g]; s_tstart[g] = tiles of the groups before g.
+// The kernel runs if the groups with more than TILE_M_MIN rows make at least
+// min_tiles tiles; it then takes the groups with more than m_min rows when
+// there are none (the wave-streaming kernel then takes every group in one
+// pass), else all groups above TILE_M_MIN.
 __device__ __forceinline__ void tile_prefix(const TArgs& a, int* s_tstart, int* s_off) {
   if (threadIdx.x >= WAVE) return;
   const int l = lane_id();
+  int t32 = 0, twide = 0;
+  for (int g = l; g < a.n_groups; g += WAVE) {
+    const int m = a.offsets[g + 1] - a.offsets[g];
+    const int t = (m + TL_M - 1) / TL_M * a.n_nt;
+    if (m > TILE_M_MIN) t32 += t;
+    if (m > a.m_min) twide += t;
+  }
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    t32 += __shfl_xor(t32, d, WAVE);
+    twide += __shfl_xor(twide, d, WAVE);
+  }
+  const int take = twide == 0 ? a.m_min : TILE_M_MIN;
   int base = 0;
   for (int g0 = 0; g0 <= a.n_groups; g0 += WAVE) {
     const int g = g0 + l;
@@ -111,13 +128,13 @@ __device__ __forceinline__ void tile_prefix(const TArgs& a, int* s_tstart, int* 
     int v = 0;
     if (g < a.n_groups) {
       const int m = a.offsets[g + 1] - a.offsets[g];
-      if (m > a.m_min) v = (m + TL_M - 1) / TL_M * a.n_nt;
+      if (m > take) v = (m + TL_M - 1) / TL_M * a.n_nt;
     }
     const int incl = wave_inclusive_scan(v);
     if (g < a.n_groups) s_tstart[g] = base + incl - v;
     base += __shfl(incl, WAVE - 1, WAVE);
   }
-  if (l == 0) s_tstart[a.n_groups] = base >= a.min_tiles ? base : 0;
+  if (l == 0) s_tstart[a.n_groups] = t32 >= a.min_tiles ? base : 0;
 }
 
 __device__ __forceinline__ uint4 tl_ldg_nt(const char* base, uint32_t off) {
@@ -479,7 +496,8 @@ size_t expert_tile_workspace_bytes(int T, int kk, int n_groups, int H, int I, in
 }
 
 void launch_expert_up_tiles(const void* x, const int32_t* sorted_pair, const int32_t* offsets, int n_groups,
-                            int T, int kk, const void* w13, int H, int I, void* A, void* ws, hipStream_t s) {
+                            int T, int kk, const void* w13, int H, int I, void* A, int m_min, void* ws,
+                            hipStream_t s) {
   TArgs a{};
   a.act = x;
   a.sorted_pair = sorted_pair;
@@ -492,12 +510,12 @@ void launch_expert_up_tiles(const void* x, const int32_t* sorted_pair, const int
   a.I_loc = I;
   a.H = H;
   a.n_nt = expert_tile_nt(true, H, I);
-  a.m_min = TILE_M_MIN;
+  a.m_min = m_min < TILE_M_MIN ? TILE_M_MIN : m_min;
   tile_launch<TMODE_UP>(a, T, ws, s);
 }
 
 void launch_expert_down_tiles(const void* A, const int32_t* offsets, int n_groups, int T, int kk,
-                              const void* w2, int H, int I, void* y_pair, void* ws, hipStream_t s) {
+                              const void* w2, int H, int I, void* y_pair, int m_min, void* ws, hipStream_t s) {
   TArgs a{};
   a.act = A;
   a.offsets = offsets;
@@ -509,7 +527,7 @@ void launch_expert_down_tiles(const void* A, const int32_t* offsets, int n_group
   a.I_loc = I;
   a.H = H;
   a.n_nt = expert_tile_nt(false, H, I);
-  a.m_min = TILE_M_MIN;
+  a.m_min = m_min < TILE_M_MIN ? TILE_M_MIN : m_min;
   tile_launch<TMODE_DOWN>(a, T, ws, s);
 }
 

@@ -49,24 +49,30 @@ void launch_expert_down(int dtype, const void* a, const int32_t* offsets, int n_
                         int kk, const void* w2, int H, int I, void* y_pair, void* ws, hipStream_t s);
 // LDS-tiled expert kernels (expert_tile.hip) for groups holding many rows:
 // for bf16 and T > TILE_T_MIN, launch_expert_up/down first launch them on
-// every group with more than TILE_M_MIN sorted rows, provided those groups
+// every group with more than m_min sorted rows (TILE_M_MIN, or
+// TILE_M_MIN_WIDE when the wave-streaming kernel holds four token tiles and
+// takes up to 64 rows in one pass), provided those groups
 // make at least expert_tile_min_tiles() tiles of TILE_ROWS token rows x
 // (up: 64 intermediate columns; down: 128 output features); the
 // wave-streaming kernel then skips exactly those groups.  Both kernels take
 // this decision on the device, from the same counts and the same formula.
 constexpr int TILE_M_MIN = 32;
+constexpr int TILE_M_MIN_WIDE = 64;
 constexpr int TILE_T_MIN = 256;
 constexpr int TILE_ROWS = 128;
 inline int expert_tile_nt(bool up, int H, int I) { return up ? (I + 63) / 64 : (H + 127) / 128; }
 int expert_tile_min_tiles();
+// The row threshold of the LDS-tiled kernels for this launch (both kernels use it).
+int expert_tile_m_min(int T, int kk, int n_groups);
 bool expert_tile_used(int T, int dtype);
 // Their workspace (split-tile counters, zero between calls, then fp32
 // partial tiles) follows the wave-streaming kernel's in the expert workspace.
 size_t expert_tile_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dtype);
 void launch_expert_up_tiles(const void* x, const int32_t* sorted_pair, const int32_t* offsets, int n_groups,
-                            int T, int kk, const void* w13, int H, int I, void* a, void* ws, hipStream_t s);
+                            int T, int kk, const void* w13, int H, int I, void* a, int m_min, void* ws,
+                            hipStream_t s);
 void launch_expert_down_tiles(const void* a, const int32_t* offsets, int n_groups, int T, int kk,
-                              const void* w2, int H, int I, void* y_pair, void* ws, hipStream_t s);
+                              const void* w2, int H, int I, void* y_pair, int m_min, void* ws, hipStream_t s);
 // weighted combine -> y (T, H); w == nullptr: every weight 1
 void launch_combine(int dtype, const void* y_pair, const int32_t* pair_pos, const float* w, int T,
                     int kk, int H, void* y, hipStream_t s);

@@ -69,6 +69,28 @@ def test_hot_expert_split_tiles(T):
     gh.check_layer(d, cfg, g)
 
 
+# Batches of 384..767 tokens with more than 24 rows per group on average take
+# the wave-streaming kernel with four token tiles (passes of 64 rows); the
+# LDS-tiled kernels then keep only groups above 64 rows.  Ragged groups of
+# 16 to 54 rows (one to four token tiles in use), K ending part-way through a
+# 512-byte chunk (H = 1568) and a hot expert of 500 rows taking eight passes.
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("T,E,k,hot", [(400, 32, 2, False), (700, 32, 2, False), (500, 16, 2, True)])
+def test_four_token_tiles(T, E, k, hot, dtype):
+    import gpu_helpers as gh
+    cfg = small(H=1568, E=E, k=k, I=736, T=T, dtype=dtype)
+    d = make_layer_inputs(cfg, T, routing="uniform", seed=T + E)
+    if hot:
+        b = np.zeros(E, dtype=np.float32)
+        b[3] = 40.0        # every token picks expert 3 first
+        d["gate_bias"] = b
+    print(f"[case] four token tiles T={T} E={E} k={k} hot={hot} {dtype}", flush=True)
+    g = gh.gpu_layer(d, cfg)
+    counts = g["counts"]
+    assert counts.max() > 32, counts  # groups past two token tiles
+    gh.check_layer(d, cfg, g)
+
+
 @pytest.mark.parametrize("n_shared,renorm", [(2, False), (1, True)])
 def test_shared_experts(n_shared, renorm):
     import gpu_helpers as gh
