@@ -8,13 +8,16 @@
 // Decode-shaped problems are HBM-bound: every weight byte must stream from
 // HBM exactly once while the token side (a few to a few dozen rows per
 // expert) is small and stays in L2.  At larger batches (bf16, T > 256) the
-// groups with more than 32 rows may have been taken by the LDS-tiled kernels
+// groups with many rows may have been taken by the LDS-tiled kernels
 // (expert_tile.hip) launched just before; this kernel re-derives that
 // decision from the same counts and skips exactly those groups.
 //
 // Work item = (group g, SUB adjacent weight tiles (1 or 4, per launch), pass
 // of 16 token rows -- 16*NT in the kernels holding NT = 2 or 4 token tiles
-// when the group has more than 16) over the full K.  A weight tile is 16 rows:
+// when the group has more than 16) over the full K.  A kernel built for four
+// token tiles also holds the two-tile body and runs it when no group it takes
+// has more than 32 rows (the first wave decides when it builds the item
+// table).  A weight tile is 16 rows:
 //   up   : 8 gate rows and the matching 8 up rows, so SiLU(gate)*up is
 //          formed in registers;
 //   down : 16 rows of W2 = 16 output features.
