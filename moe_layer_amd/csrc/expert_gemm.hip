@@ -36,8 +36,8 @@
 // HBM bandwidth, so the launch lasts as long as its most loaded CU.  The
 // grid is therefore exactly the waves that fit on the chip at once, and the
 // flattened sequence of (item, chunk) is cut into equal contiguous ranges,
-// one per wave (wave w = wv * grid + block, so a partly used grid still
-// covers every CU).  An item whose chunks fall into several waves' ranges is
+// one per wave (an eighth of them per XCD, see the kernel; a partly used
+// grid still covers every CU).  An item whose chunks fall into several waves' ranges is
 // split along K: each of those waves stores its fp32 partial tiles, and the
 // last of them to arrive (an integer counter per item; nobody waits) adds the
 // partials in K order and runs the epilogue.  Only a range's first and last
@@ -504,8 +504,24 @@ __device__ __forceinline__ void stream_body(const XArgs& a, const int* s_istart,
                                             int wv, int l, int lrow, int lq) {
   const long long Q = static_cast<long long>(uni(s_istart[a.n_groups])) * a.nck;
   const int W = static_cast<int>(min(static_cast<long long>(a.waves), (Q + MIN_CPW - 1) / MIN_CPW));
-  const int w = wv * gridDim.x + blockIdx.x;
-  if (w >= W) return;  // wave-uniform
+  // Range index.  Blocks are dealt to the 8 XCDs in turn, so XCD x holds the
+  // blocks b with b % 8 == x; it takes the contiguous ranges [x*W/8,
+  // (x+1)*W/8), first one wave of each of its blocks, then the next.  Its
+  // waves then work on neighbouring groups, whose token rows (and the
+  // down-projection's `a` rows, re-read by every item of a group) stay in that
+  // XCD's L2.  The assignment covers every range whenever the grid is a
+  // multiple of 8 (always here; otherwise wave w takes range w).
+  int w;
+  if (gridDim.x % 8 == 0) {
+    const int xcd = blockIdx.x % 8;
+    const int kx = wv * (gridDim.x / 8) + blockIdx.x / 8;
+    const int xlo = static_cast<int>(static_cast<long long>(W) * xcd / 8);
+    if (kx >= static_cast<int>(static_cast<long long>(W) * (xcd + 1) / 8) - xlo) return;  // wave-uniform
+    w = xlo + kx;
+  } else {
+    w = wv * gridDim.x + blockIdx.x;
+    if (w >= W) return;  // wave-uniform
+  }
   const long long q0 = Q * w / W;
   const long long q1 = Q * (w + 1) / W;
   if (q0 >= q1) return;
