@@ -13,8 +13,8 @@ in one launch, expert up-projection with SiLU*up, down-projection, combine:
 four launches) over one batch
 of seeded synthetic input already resident in HBM.  Weights are rotated over
 enough bit-identical copies (>= 1 GB in total) that the 256 MB Infinity
-Cache cannot serve them.  Prints ONE JSON line (rank 0; this build runs on
-one GPU only).
+Cache cannot serve them.  Prints ONE JSON line (rank 0; the benchmark runs
+on one GPU only: the path is one GPU's share of a sharded layer).
 """
 import argparse
 import hashlib
@@ -583,8 +583,9 @@ def report(wl, tm, cpu=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding is described in DESIGN.md, not run.", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
+              "it times one GPU's share (the EP and TP rank views), and no collectives are run.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
