@@ -6,10 +6,13 @@
 // Phase A -- gate GEMM.  logits[t, e] = sum_h x[t, h] W_g[e, h] + b[e] is cut
 //   into units of 16 experts x 16 tokens x one K-slice; each wave computes a
 //   unit with 16x16 MFMA tiles (lane l: expert/token row l%16, bytes
-//   16*(l/16) of each 64-byte K fragment) and writes its partial tile.  K is
-//   split into KS slices (a power of two; trailing slices may be empty) so
-//   that small batches still spread the gate matrix over many CUs.  All
-//   blocks of one 16-token tile share a counter.
+//   16*(l/16) of each 64-byte K fragment).  K is split into KS slices (a
+//   power of two; trailing slices may be empty) so that small batches still
+//   spread the gate matrix over many CUs.  With KS >= 8 a block's eight
+//   waves take eight consecutive slices of one tile and the block sums them
+//   in LDS (wave order), so only KS / 8 partial tiles go through memory;
+//   with fewer slices each wave writes its own.  All blocks of one 16-token
+//   tile share a counter.
 // Phase B -- the block that completes a token tile's counter (the last one to
 //   arrive; integer atomics, nobody waits) sums the KS partials of each of
 //   the tile's logits in slice order, adds the bias and writes the logits
@@ -24,7 +27,9 @@
 //   weight 1.  All butterfly sums are commutative at every level, so every
 //   lane holds the same bits.
 // Phase C -- the block that completes the last token tile (second counter)
-//   runs the stable counting sort of all T*kk pairs (sort.hpp).
+//   runs the stable counting sort of all T*kk pairs (sort.hpp).  A batch of
+//   one token tile (T <= 16) needs no second counter: its phase-B block
+//   writes the pair keys to LDS as it picks them and sorts from there.
 // Counters live in the caller's workspace; each finishing block resets the
 // counter it completed, so the workspace is zero again after every call.
 // Everything one block hands to another (partial tiles, logits of the
@@ -133,10 +138,16 @@ __device__ __forceinline__ float group16_sum(float v) {
 // lg: the token's E logits (LDS), E <= 16 * V.  All 16 lanes of the group
 // call this.  Weights: softmax over all E routed experts at the picks,
 // optionally renormalised over the k picks; shared experts E, E+1, ...
-// follow with weight 1.
+// follow with weight 1.  pk (LDS, nullable): the sort keys of the token's
+// k + n_shared pairs (expert - g_begin when in [0, n_groups), else n_groups).
+__device__ __forceinline__ uint16_t local_key(int id, int g_begin, int n_groups) {
+  const int g = id - g_begin;
+  return static_cast<uint16_t>((g >= 0 && g < n_groups) ? g : n_groups);
+}
 template <int V>
 __device__ __forceinline__ void group_topk(const float* lg, int E, int k, int renorm, int n_shared,
-                                           int32_t* ids, float* w) {
+                                           int32_t* ids, float* w, uint16_t* pk, int g_begin,
+                                           int n_groups) {
   const int r = lane_id() & (TK_LANES - 1);
   uint64_t key[V];  // key 0 never wins: every real key is larger
 #pragma unroll
@@ -174,14 +185,17 @@ __device__ __forceinline__ void group_topk(const float* lg, int E, int k, int re
   if (r < k) {
     st_agent(ids + r, key_expert(pick0));
     w[r] = p0 / denom;
+    if (pk) pk[r] = local_key(key_expert(pick0), g_begin, n_groups);
   }
   if (r + TK_LANES < k) {
     st_agent(ids + r + TK_LANES, key_expert(pick1));
     w[r + TK_LANES] = p1 / denom;
+    if (pk) pk[r + TK_LANES] = local_key(key_expert(pick1), g_begin, n_groups);
   }
   for (int sh = r; sh < n_shared; sh += TK_LANES) {
     st_agent(ids + k + sh, E + sh);
     w[k + sh] = 1.0f;
+    if (pk) pk[k + sh] = local_key(E + sh, g_begin, n_groups);
   }
 }
 
@@ -189,7 +203,8 @@ template <typename T, int KS>
 __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
   __shared__ int s_cnt[RT_WAVES * MAX_GROUPS];
   __shared__ int s_off[MAX_GROUPS];
-  __shared__ float s_lg[16 * MAX_E];  // the tile's logits; later the sort's 16-bit keys
+  __shared__ __align__(16) float s_lg[16 * MAX_E];  // wave partials; the tile's logits; later the sort's 16-bit keys
+  __shared__ uint16_t s_pk[16 * MAX_KK];  // sort keys of a single-tile batch
   __shared__ int s_last;              // hand-off flag
 
   // XCD-aware order: hardware deals blocks to the 8 XCDs round-robin, so
@@ -208,10 +223,15 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
   const int unit = (lb % a.bpt) * RT_WAVES + wv;
   const size_t row_bytes = static_cast<size_t>(a.H) * sizeof(T);
 
-  // ---------------- phase A: one 16x16 partial tile per wave
-  if (unit < a.n_et * KS) {
-    const int et = unit % a.n_et;
-    const int ks = unit / a.n_et;
+  // ---------------- phase A: one 16x16 partial tile per wave.  With KS >= 8
+  // the block's waves take 8 consecutive K slices of one expert tile and the
+  // block sums them (wave order) in LDS: KS / 8 partial slices reach memory.
+  constexpr bool kBlockSum = KS >= RT_WAVES;
+  const int bi = lb % a.bpt;
+  const int et_blk = bi % a.n_et;
+  if (kBlockSum || unit < a.n_et * KS) {
+    const int et = kBlockSum ? et_blk : unit % a.n_et;
+    const int ks = kBlockSum ? (bi / a.n_et) * RT_WAVES + wv : unit / a.n_et;
     const int f_begin = ks * a.kf;
     const int f_end = min(a.kfrag_total, f_begin + a.kf);  // empty for trailing slices
     float b4[4];
@@ -236,7 +256,9 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     }
     // acc[r] = D[4*lq + r][lrow]: expert et*16 + 4*lq + r, token tt*16 + lrow.
     const int t = tt * 16 + lrow;
-    if (t < a.T) {
+    if (kBlockSum) {
+      *reinterpret_cast<f32x4_t*>(s_lg + wv * 256 + 4 * l) = acc;
+    } else if (t < a.T) {
       float* dst = (KS == 1) ? a.logits + static_cast<size_t>(t) * a.E
                              : a.partial + (static_cast<size_t>(ks) * a.T + t) * a.E;
 #pragma unroll
@@ -244,6 +266,20 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
         const int e = et * 16 + 4 * lq + r;
         if (e < a.E) st_agent(dst + e, acc[r] + b4[r]);
       }
+    }
+  }
+  if (kBlockSum) {
+    __syncthreads();
+    if (tid < 256) {
+      // element tid: lane tid / 4, register tid % 4 of every wave's tile
+      float s = s_lg[tid];
+#pragma unroll
+      for (int w2 = 1; w2 < RT_WAVES; ++w2) s += s_lg[w2 * 256 + tid];
+      const int li = tid >> 2;
+      const int t = tt * 16 + (li & 15);
+      const int e = et_blk * 16 + 4 * (li >> 4) + (tid & 3);
+      if (t < a.T && e < a.E)
+        st_agent(a.partial + (static_cast<size_t>(bi / a.n_et) * a.T + t) * a.E + e, s);
     }
   }
 
@@ -256,13 +292,14 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
   const int n_lg = n_tok * a.E;
   const size_t slice = static_cast<size_t>(a.T) * a.E;
   const float* src = (KS == 1) ? a.logits : a.partial;
+  constexpr int KSP = kBlockSum ? KS / RT_WAVES : KS;  // partial slices in memory
   for (int i0 = tid; i0 < n_lg; i0 += RT_THREADS * RT_UNROLL) {
-    float part[RT_UNROLL][KS];  // every load is issued before the first add
+    float part[RT_UNROLL][KSP];  // every load is issued before the first add
 #pragma unroll
     for (int u = 0; u < RT_UNROLL; ++u) {
       const int i = min(i0 + u * RT_THREADS, n_lg - 1);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) part[u][ks] = ld_agent(src + ks * slice + static_cast<size_t>(t0) * a.E + i);
+      for (int ks = 0; ks < KSP; ++ks) part[u][ks] = ld_agent(src + ks * slice + static_cast<size_t>(t0) * a.E + i);
     }
 #pragma unroll
     for (int u = 0; u < RT_UNROLL; ++u) {
@@ -270,7 +307,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
       if (i < n_lg) {
         float s = part[u][0];
 #pragma unroll
-        for (int ks = 1; ks < KS; ++ks) s += part[u][ks];
+        for (int ks = 1; ks < KSP; ++ks) s += part[u][ks];
         if (KS > 1) {
           s += a.bias ? a.bias[i % a.E] : 0.f;
           a.logits[static_cast<size_t>(t0) * a.E + i] = s;
@@ -283,6 +320,8 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
 
   // ---------------- phase B2: top-k of the tile's tokens, 16 lanes per token
   const int kk = a.k + a.n_shared;
+  // A single token tile sorts in this block: its pair keys stay in LDS.
+  const bool one_tile = a.n_tt == 1 && a.counts != nullptr;
   {
     const int j = tid / TK_LANES;  // group-uniform
     if (j < n_tok) {
@@ -290,13 +329,21 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
       const float* lg = s_lg + j * a.E;
       int32_t* ids = a.ids + t * kk;
       float* w = a.w + t * kk;
-      if (a.E <= 4 * TK_LANES) group_topk<4>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w);
-      else if (a.E <= 8 * TK_LANES) group_topk<8>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w);
-      else if (a.E <= 16 * TK_LANES) group_topk<16>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w);
-      else group_topk<TK_MAXV>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w);
+      uint16_t* pk = one_tile ? s_pk + j * kk : nullptr;
+      if (a.E <= 4 * TK_LANES) group_topk<4>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w, pk, a.g_begin, a.n_groups);
+      else if (a.E <= 8 * TK_LANES) group_topk<8>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w, pk, a.g_begin, a.n_groups);
+      else if (a.E <= 16 * TK_LANES) group_topk<16>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w, pk, a.g_begin, a.n_groups);
+      else group_topk<TK_MAXV>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w, pk, a.g_begin, a.n_groups);
     }
   }
   if (a.counts == nullptr) return;  // routing only
+
+  if (one_tile) {
+    // the sort's first barrier orders the key writes before its passes
+    block_counting_sort<RT_WAVES, true>(a.ids, a.T * kk, a.g_begin, a.n_groups, a.counts, a.offsets,
+                                        a.sorted_pair, a.pair_pos, s_cnt, s_off, s_pk, -1);
+    return;
+  }
 
   // ---------------- hand-off: the block finishing the last tile sorts all pairs
   if (!last_to_arrive(a.ctr + a.n_tt, a.n_tt, &s_last)) return;
@@ -330,7 +377,8 @@ static RoutePlan plan_route(int T, int H, int E, int dtype) {
   p.bpt = (p.n_et * p.ks + RT_WAVES - 1) / RT_WAVES;
   p.grid = (p.n_tt * p.bpt + N_XCD - 1) / N_XCD * N_XCD;
   p.ctr_bytes = ((static_cast<size_t>(p.n_tt) + 1) * sizeof(int) + 255) & ~static_cast<size_t>(255);
-  p.partial_bytes = p.ks > 1 ? static_cast<size_t>(p.ks) * T * E * sizeof(float) : 0;
+  const int ksp = p.ks >= RT_WAVES ? p.ks / RT_WAVES : p.ks;  // partial slices in memory
+  p.partial_bytes = p.ks > 1 ? static_cast<size_t>(ksp) * T * E * sizeof(float) : 0;
   return p;
 }
 

@@ -84,6 +84,8 @@ __device__ __forceinline__ void sort_scatter(const uint16_t* s_key, const int32_
 
 // LDS needs: s_cnt[W * MAX_GROUPS] ints, s_off[MAX_GROUPS] ints and, for N <= key_cap,
 // s_key[key_cap] 16-bit keys.  Must be called by all W*64 threads of the block.
+// key_cap < 0: the caller has already written all N keys (as pair_key maps
+// them) to s_key, and ids is not read.
 template <int W, bool kCoherent>
 __device__ void block_counting_sort(const int32_t* __restrict__ ids, int N, int g_begin,
                                     int n_groups, int32_t* __restrict__ counts,
@@ -93,8 +95,8 @@ __device__ void block_counting_sort(const int32_t* __restrict__ ids, int N, int 
   const int tid = threadIdx.x;
   const int wv = tid / WAVE;
   const int l = lane_id();
-  const bool staged = N <= key_cap;
-  if (staged) {
+  const bool staged = key_cap < 0 || N <= key_cap;
+  if (key_cap >= 0 && staged) {
     // Eight loads in flight per thread (clamped addresses, no branches) before any is used.
     constexpr int U = 8;
     for (int p0 = tid; p0 < N; p0 += U * W * WAVE) {
