@@ -313,10 +313,15 @@ def test_graph_replay_matches_eager():
 
 
 @pytest.mark.parametrize("T,E,k,n_shared,H", [(3000, 64, 8, 0, 256), (8, 128, 8, 0, 4096),
-                                               (40, 64, 6, 2, 2048)])
+                                               (40, 64, 6, 2, 2048), (1, 128, 8, 0, 4096),
+                                               (13, 128, 8, 2, 4096), (16, 64, 6, 2, 2048),
+                                               (17, 128, 8, 0, 4096)])
 def test_fused_route_matches_two_calls_and_leaves_workspace_zero(T, E, k, n_shared, H):
     """One launch (routing + sort) against moe_route then moe_permute; the
-    3000-token case has more pairs than the sort stages in LDS."""
+    3000-token case has more pairs than the sort stages in LDS.  At H = 2048
+    and 4096 the gate GEMM runs 8 or 16 K slices summed per block; T <= 16
+    (one token tile, T = 1 and 13 ragged) sorts in the top-k block from LDS,
+    and T = 17 hands a one-token second tile to the sorting block."""
     import torch
 
     import gpu_helpers as gh
