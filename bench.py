@@ -1,26 +1,36 @@
-"""Benchmark: MoE-layer forward tokens/s on one MI355X, with the roofline of
-the dominant kernel and the CPU oracle timed beside it.
+"""Benchmark: MoE-layer forward tokens/s against the global batch B on one
+MI355X, with the HBM roofline fraction of every point and the CPU oracle
+timed beside the headline point.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME --tokens T --routing R]
-    python bench.py --sweep --out results.jsonl     # every batch of the EP/TP/30B workloads
+    python bench.py [--steps K] [--warmup W]          # the batch sweep (one JSON line)
+    python bench.py --workload NAME --tokens T --routing R   # one point only
     python bench.py --workload repack               # EP<->TP expert-weight repack
     python bench.py --workload dispatch [--tokens T] # EP dispatch send layout + return combine
     python bench.py --workload calibrate --steps 20  # EP/TP crossover across B + switch policy
     python bench.py --workload schedule              # Attention-DP request scheduling
+    python bench.py --ingest-counters FETCH.csv WRITE.csv --workload NAME --tokens T --routing R
 
 A step is one pass of the whole hot path (gate GEMM + softmax/top-k + permute
 in one launch, expert up-projection with SiLU*up, down-projection, combine:
-four launches) over one batch
-of seeded synthetic input already resident in HBM.  Weights are rotated over
-enough bit-identical copies (>= 1 GB in total) that the 256 MB Infinity
-Cache cannot serve them.  Prints ONE JSON line (rank 0; the benchmark runs
-on one GPU only: the path is one GPU's share of a sharded layer).
+four launches) over one batch of seeded synthetic input already resident in
+HBM.  Weights are rotated over enough bit-identical copies (>= 1 GB in total)
+that the 256 MB Infinity Cache cannot serve them.
+
+The default run times the Qwen3-235B-A22B EP rank share (16 whole experts of
+128) and TP rank share (every expert's 1/8 slice), P = 8, for B = 8 .. 2048
+under uniform and Zipf routing (the decode-step sweep of the Moebius review,
+section 2.1 and Fig. 2), then the Qwen3-30B-A3B batch sweep and the
+DeepSeek-V2-Lite layer at T = 256.  `value` is the EP share at B = 64,
+uniform routing; every point of the sweep is in `by_batch`.  Prints ONE JSON
+line (the benchmark runs on one GPU only: the path is one GPU's share of a
+sharded layer); progress goes to stderr.
 """
 import argparse
 import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -31,8 +41,18 @@ METRIC = "MoE-layer tokens/s vs batch B at 1 GPU; achieved HBM TB/s (% of peak)"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 1.0e9
-DEFAULT = ("dsv2_lite", 256, "uniform")
+HEADLINE = ("qwen3_235b_ep", 64, "uniform")
+SWEEP = ("qwen3_235b_ep", "qwen3_235b_tp")
+EXTRA_SWEEP = "qwen3_30b"
+C2 = ("dsv2_lite", 256, "uniform")
+DECODE_TARGET = 0.70          # fraction of HBM peak on the EP/TP decode points
+DECODE_BATCHES = (16, 32, 64, 128, 256)
+MEDIAN_BLOCKS = 5             # blocks of K steps behind ms_per_step_median
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "expert_up_counters.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def bench_repack(steps, warmup):
@@ -207,12 +227,14 @@ def bench_calibrate(steps, warmup):
     batches = list(get_config("qwen3_235b_ep").T_list)
     t = {"tp": [], "ep": []}
     for view in ("tp", "ep"):
+        ws = WeightSet(f"qwen3_235b_{view}", "uniform")
         for B in batches:
-            wl = Workload(f"qwen3_235b_{view}", B, "uniform")
+            wl = Workload(ws, B)
             tm = time_workload(wl, steps, warmup)
             t[view].append(tm["t_step_s"])
             del wl
-            torch.cuda.empty_cache()
+        del ws
+        torch.cuda.empty_cache()
     b_star = M.switch_crossover(batches, t["tp"], t["ep"])
     rep = bench_repack(max(3, steps // 4), 1)
     switch_s = rep["ms_per_step"] * 1e-3
@@ -328,15 +350,19 @@ def bench_schedule(steps, warmup, n_req=2048, E=8, cpu=True):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default=DEFAULT[0])
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=None)
     p.add_argument("--tokens", type=int, default=None)
     p.add_argument("--routing", default=None)
-    p.add_argument("--sweep", action="store_true", help="time every batch of the sweep workloads")
-    p.add_argument("--out", default=None, help="sweep: also append JSON lines to this file")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--graph", action="store_true", help="also time HIP-graph replay of the step")
+    p.add_argument("--no-extra", action="store_true",
+                   help="default run: leave out the Qwen3-30B sweep and the DeepSeek-V2-Lite point")
+    p.add_argument("--graph", action="store_true", help="single point: also time HIP-graph replay")
+    p.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                   help="record rocprofv3 FETCH_SIZE / WRITE_SIZE counter files of the up-projection "
+                        "for --workload/--tokens/--routing in the profiles' counter table")
+    p.add_argument("--command", default="", help="with --ingest-counters: the commands that made the files")
     return p.parse_args()
 
 
@@ -348,48 +374,69 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-class Workload:
-    """Seeded inputs on the GPU, weights replicated for cache rotation."""
+def _to_dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
 
-    def __init__(self, name, T, routing):
-        import numpy as np
-        import torch
 
+class WeightSet:
+    """One view's seeded inputs on the GPU, drawn once at the largest batch:
+    x (T_max, H) -- a batch of T tokens is its first T rows --, the gate, the
+    bias of the routing variant and the expert weights, replicated for cache
+    rotation."""
+
+    def __init__(self, name, routing):
         from moe_inputs import get_config, make_layer_inputs
         self.cfg = cfg = get_config(name)
-        self.T, self.routing = T, routing
-        self.host = make_layer_inputs(cfg, T, routing=routing)
-        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-
-        def dev(a):
-            a = np.ascontiguousarray(a)
-            if a.dtype == np.uint16:
-                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-            return torch.from_numpy(a).cuda()
-
-        self.x = dev(self.host["x"])
-        self.w_gate = dev(self.host["w_gate"])
-        self.bias = dev(self.host["gate_bias"])
-        w13, w2 = dev(self.host["w13"]), dev(self.host["w2"])
+        self.routing = routing
+        self.host = make_layer_inputs(cfg, cfg.T_max, routing=routing)
+        self.x = _to_dev(self.host["x"])
+        self.w_gate = _to_dev(self.host["w_gate"])
+        self.bias = _to_dev(self.host["gate_bias"])
+        w13, w2 = _to_dev(self.host["w13"]), _to_dev(self.host["w2"])
         wbytes = (w13.numel() + w2.numel()) * w13.element_size()
         self.copies = max(1, math.ceil(ROTATE_BYTES / wbytes))
         self.w13 = [w13] + [w13.clone() for _ in range(self.copies - 1)]
         self.w2 = [w2] + [w2.clone() for _ in range(self.copies - 1)]
         self.g_begin = self.host["g_begin"]
-        self.dtype = tdt
-        self.elem = 2 if cfg.dtype == "bf16" else 4
+        self.rank = self.host["rank"]
+
+
+class Workload:
+    """A batch of T tokens on a WeightSet, with its output buffers."""
+
+    def __init__(self, ws, T):
+        import torch
+
         import moe_layer_amd
-        self.bufs = moe_layer_amd.MoeLayerBuffers.allocate(
-            T, cfg.H, cfg.E, cfg.kk, cfg.n_groups, cfg.I_local, tdt)
+        self.ws, self.cfg, self.T, self.routing = ws, ws.cfg, T, ws.routing
+        self.x = ws.x[:T]
+        self.w_gate, self.bias, self.g_begin = ws.w_gate, ws.bias, ws.g_begin
+        self.w13, self.w2, self.copies = ws.w13, ws.w2, ws.copies
+        self.dtype = torch.bfloat16 if self.cfg.dtype == "bf16" else torch.float32
+        self.elem = 2 if self.cfg.dtype == "bf16" else 4
+        c = self.cfg
+        self.bufs = moe_layer_amd.MoeLayerBuffers.allocate(T, c.H, c.E, c.kk, c.n_groups, c.I_local,
+                                                           self.dtype)
+
+    def host_inputs(self):
+        d = dict(self.ws.host)
+        d["x"] = d["x"][:self.T]
+        return d
 
     def describe(self):
         c = self.cfg
         return {
-            "workload": f"{c.name} T={self.T} {self.routing} ({c.view} view)",
+            "workload": f"{c.name} B={self.T} {self.routing} ({c.view} view"
+                        + (f", rank {self.ws.rank} of {c.P}" if c.view != "full" else "") + ")",
             "tokens": self.T, "hidden": c.H, "experts": c.E, "top_k": c.k,
             "renormalised": c.renorm, "shared_experts": c.n_shared, "intermediate_local": c.I_local,
-            "groups_held": c.n_groups, "view": c.view, "ranks_P": c.P, "routing": self.routing,
-            "weight_copies_rotated": self.copies,
+            "groups_held": c.n_groups, "view": c.view, "ranks_P": c.P, "rank": self.ws.rank,
+            "routing": self.routing, "weight_copies_rotated": self.copies,
         }
 
 
@@ -416,7 +463,9 @@ def run_step(wl, i, events=None, up_events=None):
 
 
 def algorithmic(wl):
-    """Bytes and flops the method must move / do (intermediates excluded)."""
+    """Bytes and flops the method must move / do (intermediates excluded):
+    the gate matrix, x, y and the W13 + W2 of every touched group (touched =
+    a non-zero count on the GPU's own routing)."""
     c, s, T = wl.cfg, wl.elem, wl.T
     counts = wl.bufs.counts.cpu().numpy()
     touched = int((counts > 0).sum())
@@ -434,20 +483,26 @@ def algorithmic(wl):
 def time_workload(wl, steps, warmup, graph=False):
     """K timed steps between two synchronisations, with nothing but the four
     calls in the loop: an event record is a queue packet of its own and costs
-    the GPU ~5 us of idle time, so events would inflate the step.  A second
-    timed pass of K identical steps records two HIP events per step on the
-    launch stream around the up-projection: their mean is the dominant
-    kernel's duration.  A third pass with events around every call gives the
-    other kernels' durations (those include the event packets)."""
+    the GPU ~5 us of idle time, so events would inflate the step.  Then
+    MEDIAN_BLOCKS - 1 more blocks of K steps (the median of the block means
+    is ms_per_step_median).  A further pass of K steps records two HIP events
+    per step on the launch stream around the up-projection: their mean is the
+    dominant kernel's duration.  A last pass with events around every call
+    gives the other kernels' durations (those include the event packets).
+    With graph=True the step is also captured in HIP graphs (one per weight
+    copy) and K replays are timed the same way."""
     import torch
     for i in range(warmup):
         run_step(wl, i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        run_step(wl, i)
-    torch.cuda.synchronize()
-    t_step = (time.perf_counter() - t0) / steps
+    blocks = []
+    for blk in range(MEDIAN_BLOCKS):
+        t0 = time.perf_counter()
+        for i in range(steps):
+            run_step(wl, i)
+        torch.cuda.synchronize()
+        blocks.append((time.perf_counter() - t0) / steps)
+    t_step = blocks[0]          # the K timed steps
     up = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda.synchronize()
@@ -463,7 +518,8 @@ def time_workload(wl, steps, warmup, graph=False):
     names = ("route_permute", "expert_up", "expert_down", "combine")
     per = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps * 1e3
            for j, n in enumerate(names)}
-    out = {"t_step_s": t_step, "t_up_us": t_up_us, "kernels_us": per}
+    out = {"t_step_s": t_step, "t_step_median_s": statistics.median(blocks), "t_up_us": t_up_us,
+           "kernels_us": per, "steps": steps, "warmup": warmup}
     if graph:
         out["t_step_graph_s"] = time_graph(wl, steps)
     return out
@@ -489,35 +545,81 @@ def time_graph(wl, steps):
     for i in range(steps):
         graphs[i % wl.copies].replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    t = (time.perf_counter() - t0) / steps
+    del graphs
+    return t
 
 
-def measured_traffic():
-    """HBM bytes per up-projection launch from committed rocprofv3 counters
-    (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by what the
-    same counter reads for the repack copy of known size), or None when
-    absent or taken on a different kernel source."""
+def _load_counters():
     try:
         with open(PROFILE_COUNTERS) as f:
-            c = json.load(f)
+            return json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("source_sha") != kernel_source_sha():
+
+
+def measured_traffic(name, T, routing):
+    """HBM bytes per up-projection launch of exactly this workload, batch and
+    routing, from committed rocprofv3 counters (FETCH_SIZE and WRITE_SIZE in
+    KiB per dispatch, each scaled by what the same counter reads for a copy of
+    known size), or None when no entry matches or the entry was taken on a
+    different kernel source."""
+    c = _load_counters()
+    if not c:
         return None
-    return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
+    sha = kernel_source_sha()
+    for e in c.get("entries", []):
+        if (e.get("workload"), e.get("T"), e.get("routing"), e.get("source_sha")) == (name, T, routing, sha):
+            return (e["fetch_kib"] * c["fetch_scale"] + e["write_kib"] * c["write_scale"]) * 1024.0
+    return None
+
+
+def ingest_counters(fetch_csv, write_csv, name, T, routing, command):
+    """Record the up-projection's mean FETCH_SIZE and WRITE_SIZE per dispatch
+    (rocprofv3 --pmc counter_collection.csv files, one counter per run) for
+    this workload in the counter table bench.py reads."""
+    import csv
+
+    def mean_kib(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                kname = row.get("Kernel_Name", "")
+                if "expert_wave_kernel" not in kname or ", 0, " not in kname:
+                    continue   # the up-projection is expert_wave_kernel<T, 0, ...>
+                if row.get("Counter_Name") != counter:
+                    continue
+                vals.setdefault(row.get("Dispatch_Id"), 0.0)
+                vals[row.get("Dispatch_Id")] += float(row["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"no {counter} rows of the up-projection in {path}")
+        return sum(vals.values()) / len(vals), len(vals)
+
+    fk, nf = mean_kib(fetch_csv, "FETCH_SIZE")
+    wk, nw = mean_kib(write_csv, "WRITE_SIZE")
+    c = _load_counters() or {}
+    c.setdefault("fetch_scale", 1.9994)
+    c.setdefault("write_scale", 0.9997)
+    entries = [e for e in c.get("entries", []) if (e.get("workload"), e.get("T"), e.get("routing")) != (name, T, routing)]
+    entries.append({"workload": name, "T": T, "routing": routing, "kernel": "moe_expert_up (expert_wave_kernel<bf16, UP, ...>)",
+                    "source_sha": kernel_source_sha(), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                    "dispatches": min(nf, nw), "commands": command})
+    c["entries"] = sorted(entries, key=lambda e: (e["workload"], e["routing"], e["T"]))
+    with open(PROFILE_COUNTERS, "w") as f:
+        json.dump(c, f, indent=1)
+        f.write("\n")
+    print(json.dumps(c["entries"][-1]))
 
 
 def cpu_baseline(wl, budget_s=10.0):
     """The oracle (numpy float64) on the same inputs, on this host's cores."""
-    import numpy as np
-
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - reporting only
         cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    c, d = wl.cfg, wl.host
+    c, d = wl.cfg, wl.host_inputs()
     runs, t_total = 0, 0.0
     while runs == 0 or (t_total < budget_s and runs < 30):
         t0 = time.perf_counter()
@@ -527,11 +629,62 @@ def cpu_baseline(wl, budget_s=10.0):
         runs += 1
     t = t_total / runs
     return {"value": wl.T / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"whole layer, {wl.T} tokens, {runs} run(s), mean {t:.2f} s per pass "
+            "sample": f"whole layer of {wl.describe()['workload']}, {runs} run(s), mean {t:.2f} s per pass "
                       f"(numpy float64, BLAS threads={cores}, CPUs visible={len(os.sched_getaffinity(0))})"}
 
 
+def copy_ceiling(nbytes=1 << 30, reps=20):
+    """A plain device copy (torch's copy kernel) of nbytes: read + write rate,
+    the measured ceiling beside the 8 TB/s peak."""
+    import torch
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    gbs = 2 * nbytes / t / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": "torch copy_ of a 1 GiB bf16 tensor (read + write)", "GBs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "us": round(t * 1e6, 1)}
+
+
+def point(wl, tm):
+    """One sweep point: tokens/s, step times, the up-projection's and the
+    layer's HBM fractions (algorithmic bytes / time)."""
+    a = algorithmic(wl)
+    t, tg = tm["t_step_s"], tm.get("t_step_graph_s")
+    up_gbs = a["up_bytes"] / (tm["t_up_us"] * 1e-6) / 1e9
+    row = {
+        "view": wl.cfg.view, "routing": wl.routing, "B": wl.T,
+        "tokens_per_s": round(wl.T / t, 1),
+        "ms_per_step": round(t * 1e3, 5),
+        "ms_per_step_median": round(tm["t_step_median_s"] * 1e3, 5),
+        "graph_ms_per_step": round(tg * 1e3, 5) if tg else None,
+        "layer_hbm_frac": round(a["layer_bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_hbm_frac_median": round(a["layer_bytes"] / tm["t_step_median_s"] / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_mfma_frac": round(a["layer_flops"] / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "up_frac": round(up_gbs / HBM_PEAK_GBS, 4),
+        "up_us": round(tm["t_up_us"], 2),
+        "layer_bytes": a["layer_bytes"], "up_bytes": a["up_bytes"],
+        "touched_groups": a["touched"], "kept_pairs": a["kept"],
+        "kernels_us": {k: round(v, 2) for k, v in tm["kernels_us"].items()},
+        "up_traffic": measured_traffic(wl.cfg.name, wl.T, wl.routing),
+    }
+    if wl.cfg.view == "ep":
+        row["rank"] = wl.ws.rank
+    return row
+
+
 def report(wl, tm, cpu=None):
+    """The full line of one point (the headline, or a single-point run)."""
     a = algorithmic(wl)
     t = tm["t_step_s"]
     t_up = tm["t_up_us"] * 1e-6
@@ -557,7 +710,7 @@ def report(wl, tm, cpu=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic(wl.cfg.name, wl.T, wl.routing),
             "algorithmic_bytes_per_launch": a["up_bytes"],
         },
         "layer": {
@@ -570,6 +723,7 @@ def report(wl, tm, cpu=None):
             "kept_pairs": a["kept"],
             "kernels_us": {k: round(v, 2) for k, v in tm["kernels_us"].items()},
             "expert_up_us_timed_region": round(tm["t_up_us"], 2),
+            "ms_per_step_median": tm["t_step_median_s"] * 1e3,
         },
         "cpu_baseline": cpu,
     }
@@ -580,8 +734,73 @@ def report(wl, tm, cpu=None):
     return line
 
 
+def bench_default(steps, warmup, cpu=True, extra=True):
+    """The batch sweep on the Qwen3-235B-A22B EP and TP rank shares (and,
+    with extra, the Qwen3-30B-A3B sweep and the DeepSeek-V2-Lite layer)."""
+    import torch
+    from moe_inputs import get_config
+    rows, extra_rows, head, c2 = [], [], None, None
+    plan = [(name, r) for name in SWEEP for r in get_config(name).routing]
+    if extra:
+        plan += [(EXTRA_SWEEP, r) for r in get_config(EXTRA_SWEEP).routing]
+    for name, routing in plan:
+        ws = WeightSet(name, routing)
+        for T in ws.cfg.T_list:
+            wl = Workload(ws, T)
+            tm = time_workload(wl, steps, warmup, graph=True)
+            row = point(wl, tm)
+            (rows if name in SWEEP else extra_rows).append(row)
+            log(f"{name} {routing} B={T}: {row['ms_per_step'] * 1e3:.1f} us/step, layer "
+                f"{row['layer_hbm_frac']:.3f}, up {row['up_frac']:.3f} of HBM peak")
+            if (name, T, routing) == HEADLINE:
+                head = report(wl, tm, cpu_baseline(wl) if cpu else None)
+                log(f"headline cpu baseline: {head['cpu_baseline']}")
+            del wl
+        del ws
+        torch.cuda.empty_cache()
+    if extra:
+        ws = WeightSet(C2[0], C2[2])
+        wl = Workload(ws, C2[1])
+        tm = time_workload(wl, steps, warmup, graph=True)
+        c2 = point(wl, tm)
+        c2["workload"] = wl.describe()["workload"]
+        c2["up_traffic"] = measured_traffic(*C2)
+        log(f"{C2}: {c2['ms_per_step'] * 1e3:.1f} us/step, layer {c2['layer_hbm_frac']:.3f}")
+        del wl, ws
+        torch.cuda.empty_cache()
+    line = head
+    line["config"] = {
+        "workload": "Qwen3-235B-A22B-shaped EP rank share (16 of 128 experts, W13 (16,3072,4096)) and TP "
+                    "rank share (128 experts sharded I/8, W13 (128,384,4096)), P=8, layer step across "
+                    "global batch B=8..2048, uniform and Zipf(1.2) routing; value = EP share, B=64, uniform",
+        "headline": head["config"],
+        "batches": list(get_config(SWEEP[0]).T_list),
+        "views": ["ep", "tp"],
+        "routings": ["uniform", "zipf"],
+    }
+    line["by_batch"] = rows
+    dec = [r for r in rows if r["routing"] == "uniform" and r["B"] in DECODE_BATCHES]
+    line["decode_target"] = {
+        "points": "EP and TP shares, uniform routing, B=" + ",".join(map(str, DECODE_BATCHES)),
+        "target_layer_hbm_frac": DECODE_TARGET,
+        "min_layer_hbm_frac": min(r["layer_hbm_frac"] for r in dec),
+        "min_layer_hbm_frac_median": min(r["layer_hbm_frac_median"] for r in dec),
+        "met": all(r["layer_hbm_frac"] >= DECODE_TARGET for r in dec),
+    }
+    if extra:
+        line["qwen3_30b_by_batch"] = extra_rows
+        line["dsv2_lite"] = c2
+    line["copy_ceiling"] = copy_ceiling()
+    return line
+
+
 def main():
     args = parse()
+    if args.ingest_counters:
+        if not (args.workload and args.tokens and args.routing):
+            raise SystemExit("--ingest-counters needs --workload, --tokens and --routing")
+        ingest_counters(*args.ingest_counters, args.workload, args.tokens, args.routing, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "it times one GPU's share (the EP and TP rank views), and no collectives are run.",
@@ -594,25 +813,10 @@ def main():
     import moe_layer_amd
     moe_layer_amd.lib()
 
-    if args.sweep:
-        from moe_inputs import get_config
-        out = open(args.out, "a") if args.out else None
-        for name in ("qwen3_235b_ep", "qwen3_235b_tp", "qwen3_30b"):
-            cfg = get_config(name)
-            for routing in cfg.routing:
-                for T in cfg.T_list:
-                    wl = Workload(name, T, routing)
-                    tm = time_workload(wl, args.steps, args.warmup, graph=args.graph)
-                    tm.update(steps=args.steps, warmup=args.warmup)
-                    line = json.dumps(report(wl, tm))
-                    print(line, flush=True)
-                    if out:
-                        out.write(line + "\n")
-                        out.flush()
-                    del wl
-                    torch.cuda.empty_cache()
+    if args.workload is None:
+        print(json.dumps(bench_default(args.steps, args.warmup, cpu=not args.no_cpu_baseline,
+                                       extra=not args.no_extra)), flush=True)
         return
-
     if args.workload == "repack":
         print(json.dumps(bench_repack(args.steps, args.warmup)), flush=True)
         return
@@ -628,14 +832,12 @@ def main():
               flush=True)
         return
 
-    name = args.workload
     from moe_inputs import get_config
-    cfg = get_config(name)
-    T = args.tokens or (DEFAULT[1] if name == DEFAULT[0] else cfg.T_list[-1])
+    cfg = get_config(args.workload)
+    T = args.tokens or cfg.T_list[-1]
     routing = args.routing or cfg.routing[0]
-    wl = Workload(name, T, routing)
+    wl = Workload(WeightSet(args.workload, routing), T)
     tm = time_workload(wl, args.steps, args.warmup, graph=args.graph)
-    tm.update(steps=args.steps, warmup=args.warmup)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
     print(json.dumps(report(wl, tm, cpu)), flush=True)
 

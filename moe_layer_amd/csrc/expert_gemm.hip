@@ -73,6 +73,8 @@
 // group's count repeat a real row and are never stored; fragments past the
 // end of K are zero on both sides.  Every output element is written by
 // exactly one lane.
+#include <algorithm>
+
 #include "common.hpp"
 #include "moe_internal.h"
 
@@ -809,17 +811,11 @@ size_t expert_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dty
 
 template <typename T, int MODE, int NT, int SUB, bool FULLK>
 static int resident_blocks() {
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&expert_wave_kernel<T, MODE, NT, SUB, FULLK>), XW_WAVES * WAVE, 0) !=
-            hipSuccess || n < 1)
-      n = 1;
-    // The streaming rate drops with more than two blocks of four waves per
-    // CU (more concurrent row streams); kernels with two token tiles fit one.
-    per_cu = n < 2 ? n : 2;
-  }
+  // The streaming rate drops with more than two blocks of four waves per CU
+  // (more concurrent row streams); kernels with two token tiles fit one.
+  static const int per_cu = std::min(
+      2, kernel_blocks_per_cu(reinterpret_cast<const void*>(&expert_wave_kernel<T, MODE, NT, SUB, FULLK>),
+                              XW_WAVES * WAVE));
   long long g = static_cast<long long>(device_cu_count()) * per_cu;
   if (g * XW_WAVES > MAX_WAVES) g = MAX_WAVES / XW_WAVES;
   return static_cast<int>(g);

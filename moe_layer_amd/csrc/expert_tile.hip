@@ -440,14 +440,8 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
 
 template <int MODE>
 static int tile_resident_blocks() {
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&expert_tile_kernel<MODE>), TL_THREADS, 0) != hipSuccess || n < 1)
-      n = 1;
-    per_cu = n;
-  }
+  static const int per_cu =
+      kernel_blocks_per_cu(reinterpret_cast<const void*>(&expert_tile_kernel<MODE>), TL_THREADS);
   return device_cu_count() * per_cu;
 }
 

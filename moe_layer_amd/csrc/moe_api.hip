@@ -5,18 +5,18 @@
 
 namespace moe {
 
-static int g_cu_count[64];
-
 int device_cu_count() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (g_cu_count[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    g_cu_count[dev] = n;
-  }
-  return g_cu_count[dev];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  return n;
+}
+
+int kernel_blocks_per_cu(const void* kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
+  return n;
 }
 
 }  // namespace moe
@@ -96,6 +96,9 @@ int check_route(const void* x, const void* w_gate, const float* gate_bias, int T
                 size_t ws_bytes) {
   if (T < 0 || H < 1 || E < 1 || k < 1 || n_shared < 0 || k > E || !dtype_ok(dtype)) return MOE_EINVAL;
   if (E > MAX_E || k > MAX_K || k + n_shared > MAX_KK || !k_len_ok(H, dtype)) return MOE_EUNSUPPORTED;
+  // pair indices and the sort length are 32-bit; so is the launch grid
+  if (static_cast<long long>(T) * (k + n_shared) > (1LL << 30) || !route_fits(T, H, E, dtype))
+    return MOE_EUNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w_gate || !logits || !topk_ids || !topk_w) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(w_gate) || !aligned4(logits) || !aligned4(topk_ids) ||

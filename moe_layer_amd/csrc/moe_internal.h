@@ -16,13 +16,21 @@ constexpr int MAX_K = 32;         // routed picks per token
 constexpr int MAX_KK = 64;        // routed + shared slots per token
 constexpr int MAX_P = 64;         // peers in a repack
 
+// Compute units of the current device (queried on every call).
 int device_cu_count();
+// Blocks of `threads` threads of `kernel` resident on one compute unit (at
+// least 1).  It depends only on the code object, so launchers keep it in a
+// function-local constant: initialised once (thread-safely, as C++ does for
+// such statics) and never written again.
+int kernel_blocks_per_cu(const void* kernel, int threads);
 
 // gate GEMM + softmax + top-k (+ renorm, + shared slots) in one launch, and,
 // when `counts` is non-null, the stable permutation of the pairs as well.
 // ws: route_workspace_bytes() bytes whose counter head is zero on entry (and
 // is left zero).
 size_t route_workspace_bytes(int T, int H, int E, int dtype);
+// whether the launch grid of these sizes has a 32-bit block count
+bool route_fits(int T, int H, int E, int dtype);
 void launch_route(int dtype, const void* x, const void* wg, const float* bias, float* logits,
                   int32_t* ids, float* w, int T, int H, int E, int k, int renorm, int n_shared,
                   void* ws, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,

@@ -257,17 +257,12 @@ __global__ __launch_bounds__(RP_WAVES * WAVE) void repack2_kernel(RepackArgs a) 
 
 template <typename K>
 static int rp_per_cu(K kernel) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kernel), RP_WAVES * WAVE, 0) !=
-          hipSuccess || n < 1)
-    n = 1;
-  return n;
+  return kernel_blocks_per_cu(reinterpret_cast<const void*>(kernel), RP_WAVES * WAVE);
 }
 
 template <bool INV, int PATH>
 static void launch_repack2(const RepackArgs& a, hipStream_t s) {
-  static int per_cu = 0;
-  if (per_cu == 0) per_cu = rp_per_cu(&repack2_kernel<INV, PATH>);
+  static const int per_cu = rp_per_cu(&repack2_kernel<INV, PATH>);
   long long g = static_cast<long long>(device_cu_count()) * per_cu;
   if (g > (a.rows2 + RP_WAVES - 1) / RP_WAVES) g = (a.rows2 + RP_WAVES - 1) / RP_WAVES;
   hipLaunchKernelGGL((repack2_kernel<INV, PATH>), dim3(static_cast<unsigned>(g > 0 ? g : 1)), dim3(RP_WAVES * WAVE), 0,
@@ -300,8 +295,7 @@ static void launch_repack(int dtype, void* w13, void* w2, int E_local, int H, in
   a.Ip = I / P;
   a.seg2 = a.Ip * eb / 16;
   a.P = P;
-  static int per_cu13 = 0;
-  if (per_cu13 == 0) per_cu13 = rp_per_cu(&repack13_kernel<INV>);
+  static const int per_cu13 = rp_per_cu(&repack13_kernel<INV>);
   const long long units13 = a.rows13 * ((a.row13 + RP_STEP - 1) / RP_STEP);
   long long g13 = static_cast<long long>(device_cu_count()) * per_cu13;
   if (g13 > (units13 + RP_WAVES - 1) / RP_WAVES) g13 = (units13 + RP_WAVES - 1) / RP_WAVES;

@@ -382,6 +382,15 @@ static RoutePlan plan_route(int T, int H, int E, int dtype) {
   return p;
 }
 
+bool route_fits(int T, int H, int E, int dtype) {
+  if (T <= 0) return true;
+  const long long n_tt = (static_cast<long long>(T) + 15) / 16;
+  const long long n_et = (E + 15) / 16;
+  // the fewest K slices any plan takes is 1: bpt >= ceil(n_et / 8); the most is RT_MAX_KS
+  const long long bpt = (n_et * RT_MAX_KS + RT_WAVES - 1) / RT_WAVES;
+  return n_tt * bpt + N_XCD <= 0x7fffffffLL && static_cast<long long>(H) * (dtype == 1 ? 2 : 4) / FRAG_BYTES > 0;
+}
+
 size_t route_workspace_bytes(int T, int H, int E, int dtype) {
   if (T <= 0) return 0;
   const RoutePlan p = plan_route(T, H, E, dtype);

@@ -93,6 +93,8 @@ def route_permute(L, T=4, H=256, E=8, k=2, g_begin=0, n_groups=8, counts=FAKE, w
     (dict(k=2, ns=63), MOE_EUNSUPPORTED),    # k + n_shared > 64
     (dict(H=100), MOE_EUNSUPPORTED),         # not whole 64-byte K chunks
     (dict(H=1 << 20), MOE_EUNSUPPORTED),     # rows over 1 MiB
+    (dict(T=(1 << 27) + 1, k=8), MOE_EUNSUPPORTED),      # T * kk over 2^30 pairs
+    (dict(T=1 << 30, E=512, k=1), MOE_EUNSUPPORTED),      # 2^30 pairs, but over 2^31 blocks
     (dict(ws=None), MOE_EWORKSPACE),
     (dict(ws=MISALIGNED), MOE_EWORKSPACE),
     (dict(ws_bytes=0), MOE_EWORKSPACE),
@@ -108,6 +110,7 @@ def test_route_rejects(L, kw, status):
     (dict(counts=None), MOE_EINVAL),
     (dict(ws_bytes=16), MOE_EWORKSPACE),
     (dict(x=None), MOE_EINVAL),
+    (dict(T=(1 << 29) + 1), MOE_EUNSUPPORTED),   # T * kk over 2^30 pairs
 ])
 def test_route_permute_rejects(L, kw, status):
     assert route_permute(L, **kw) == status

@@ -100,6 +100,31 @@ def test_shared_experts(n_shared, renorm):
     gh.check_layer(d, cfg, gh.gpu_layer(d, cfg))
 
 
+# The routing limits the ABI advertises: E up to 512 experts (lanes holding
+# 8, 16 or 32 candidate keys each) and k up to 32 picks (rounds 16..31 go to
+# a lane's second pick register), with and without shared slots, an expert
+# count that is not a multiple of 16, fp32 storage, one and several token
+# tiles, and both the one-launch and the two-call routing.  Seeds chosen so
+# that no token's k-th and (k+1)-th logits lie within 1e-4 of each other.
+@pytest.mark.parametrize("E,k,n_shared,dtype,T,fused", [
+    (192, 17, 0, "bf16", 40, True),
+    (512, 32, 0, "bf16", 33, True),
+    (510, 32, 2, "bf16", 16, True),     # one token tile: keys sorted from LDS; 512 groups
+    (512, 32, 0, "bf16", 33, False),    # moe_route + moe_permute
+    (200, 20, 0, "fp32", 24, True),     # 13 expert tiles, the last half full
+    (256, 32, 0, "bf16", 8, True),
+    (384, 24, 1, "bf16", 70, False),
+])
+def test_wide_routing(E, k, n_shared, dtype, T, fused):
+    import gpu_helpers as gh
+    cfg = small(H=256, E=E, k=k, I=64, renorm=n_shared == 0, n_shared=n_shared, dtype=dtype, T=T)
+    d = make_layer_inputs(cfg, T, routing="uniform", seed=100)
+    print(f"[case] wide routing E={E} k={k} shared={n_shared} {dtype} T={T} fused={fused}", flush=True)
+    g = gh.gpu_layer(d, cfg, fused=fused)
+    assert g["topk_ids"].shape == (T, k + n_shared)
+    gh.check_layer(d, cfg, g)
+
+
 def test_k_equals_E():
     import gpu_helpers as gh
     cfg = small(E=8, k=8, T=20)
