@@ -120,6 +120,29 @@ int moe_route_permute(const void* x, const void* w_gate, const float* gate_bias,
                       hipStream_t stream);
 
 /*
+ * moe_route_permute_noalloc -- moe_route_permute without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * routing's scratch (per-token-tile counters, K-slice partial logits) is a
+ * fixed 16 MiB device array inside the library, one copy per GPU, held until
+ * the process ends; its address is looked up once per device.  Nothing is
+ * allocated and no allocating routine is called.  Each call first clears the
+ * counters it uses with a small fill kernel on `stream`, then runs the same
+ * kernel as moe_route_permute, so its outputs are bit-identical to that
+ * call's.  All calls on one GPU share the array: calls that overlap in time
+ * (several streams or host threads) race on it and must be serialised by the
+ * caller.  Arguments, outputs and limits are those of moe_route_permute;
+ * shapes whose moe_route_workspace_bytes exceeds 16 MiB are rejected with
+ * MOE_EWORKSPACE (every batch up to millions of tokens fits: the partial
+ * logits never exceed about 8 MB), and a failed address lookup returns
+ * MOE_EHIP with nothing enqueued.
+ */
+int moe_route_permute_noalloc(const void* x, const void* w_gate, const float* gate_bias, int T, int H, int E,
+                              int k, int renorm, int n_shared, int dtype, float* logits, int32_t* topk_ids,
+                              float* topk_w, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_pair, int32_t* pair_pos, hipStream_t stream);
+
+/*
  * moe_permute -- expert counts, offsets and the stable argsort of the
  * (token, slot) pairs by expert group (the token reorder of the Sem-MoE
  * notes, Key design 4).  Pair p = t*kk + j; its group is topk_ids[p] - g_begin

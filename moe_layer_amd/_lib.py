@@ -21,7 +21,7 @@ MOE_OP_EXPERT_UP, MOE_OP_EXPERT_DOWN = 5, 6
 
 EXPORTED = (
     "moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route_workspace_bytes",
-    "moe_route", "moe_route_permute", "moe_permute", "moe_grouped_gemm", "moe_expert_up",
+    "moe_route", "moe_route_permute", "moe_route_permute_noalloc", "moe_permute", "moe_grouped_gemm", "moe_expert_up",
     "moe_expert_down", "moe_combine", "moe_repack_ep_to_tp", "moe_repack_tp_to_ep", "moe_dispatch",
     "moe_switch_init", "moe_switch_step", "moe_switch_crossover", "moe_schedule_workspace_bytes",
     "moe_schedule_requests",
@@ -82,6 +82,9 @@ def lib():
     L.moe_route_permute.restype = _i
     L.moe_route_permute.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i,
                                     _p, _p, _p, _p, _p, _sz, _p]
+    L.moe_route_permute_noalloc.restype = _i
+    L.moe_route_permute_noalloc.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i,
+                                            _p, _p, _p, _p, _p]
     L.moe_permute.restype = _i
     L.moe_permute.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p]
     L.moe_grouped_gemm.restype = _i
@@ -199,6 +202,22 @@ def moe_route_permute(x, w_gate, gate_bias, k, renorm, n_shared, logits, topk_id
         _ptr(pair_pos, "pair_pos", torch.int32, (T * kk,)), _ptr(ws, "ws"),
         ws.numel() * ws.element_size(), _stream(stream))
     _check("moe_route_permute", st)
+
+
+def moe_route_permute_noalloc(x, w_gate, gate_bias, k, renorm, n_shared, logits, topk_ids, topk_w,
+                              g_begin, n_groups, counts, offsets, sorted_pair, pair_pos, stream=None):
+    """moe_route_permute with the library's fixed per-GPU scratch instead of a
+    workspace (nothing is allocated; calls on one GPU must not overlap)."""
+    px, pw, pb, T, H, E, pl, pi, pww = _route_common(x, w_gate, gate_bias, k, n_shared, logits,
+                                                     topk_ids, topk_w)
+    kk = k + n_shared
+    st = lib().moe_route_permute_noalloc(
+        px, pw, pb, T, H, E, k, int(bool(renorm)), n_shared, _dtype_code(x), pl, pi, pww, g_begin,
+        n_groups, _ptr(counts, "counts", torch.int32, (n_groups,)),
+        _ptr(offsets, "offsets", torch.int32, (n_groups + 1,)),
+        _ptr(sorted_pair, "sorted_pair", torch.int32, (T * kk,)),
+        _ptr(pair_pos, "pair_pos", torch.int32, (T * kk,)), _stream(stream))
+    _check("moe_route_permute_noalloc", st)
 
 
 def moe_permute(topk_ids, g_begin, n_groups, counts, offsets, sorted_pair, pair_pos, stream=None):

@@ -25,7 +25,7 @@ using namespace moe;
 
 namespace {
 
-constexpr int ABI_VERSION = 7;
+constexpr int ABI_VERSION = 8;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -142,6 +142,33 @@ int moe_route_permute(const void* x, const void* w_gate, const float* gate_bias,
   }
   launch_route(dtype, x, w_gate, gate_bias, logits, topk_ids, topk_w, T, H, E, k, renorm ? 1 : 0,
                n_shared, ws, g_begin, n_groups, counts, offsets, sorted_pair, pair_pos, stream);
+  return launched();
+}
+
+int moe_route_permute_noalloc(const void* x, const void* w_gate, const float* gate_bias, int T, int H, int E,
+                              int k, int renorm, int n_shared, int dtype, float* logits, int32_t* topk_ids,
+                              float* topk_w, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_pair, int32_t* pair_pos, hipStream_t stream) {
+  // The checks of moe_route_permute, with the fixed scratch standing in for
+  // the workspace: its size limit is the scratch size (MOE_EWORKSPACE above).
+  int st = check_route(x, w_gate, gate_bias, T, H, E, k, n_shared, dtype, logits, topk_ids, topk_w,
+                       reinterpret_cast<void*>(256), ~size_t(0));
+  if (st != MOE_OK) return st;
+  if (T > 0 && route_workspace_bytes(T, H, E, dtype) > ROUTE_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  if (g_begin < 0 || n_groups < 1) return MOE_EINVAL;
+  if (n_groups > MAX_GROUPS) return MOE_EUNSUPPORTED;
+  if (!counts || !offsets || !aligned4(counts) || !aligned4(offsets)) return MOE_EINVAL;
+  if (T > 0 && (!sorted_pair || !pair_pos || !aligned4(sorted_pair) || !aligned4(pair_pos)))
+    return MOE_EINVAL;
+  if (T == 0) {
+    launch_permute(topk_ids, 0, k + n_shared, g_begin, n_groups, counts, offsets, sorted_pair,
+                   pair_pos, stream);
+    return launched();
+  }
+  if (launch_route_permute_scratch(dtype, x, w_gate, gate_bias, logits, topk_ids, topk_w, T, H, E, k,
+                                   renorm ? 1 : 0, n_shared, g_begin, n_groups, counts, offsets, sorted_pair,
+                                   pair_pos, stream) != 0)
+    return MOE_EHIP;
   return launched();
 }
 

@@ -31,6 +31,16 @@ int kernel_blocks_per_cu(const void* kernel, int threads);
 size_t route_workspace_bytes(int T, int H, int E, int dtype);
 // whether the launch grid of these sizes has a 32-bit block count
 bool route_fits(int T, int H, int E, int dtype);
+// The allocation-free routing: the workspace is a fixed device array of
+// ROUTE_SCRATCH_BYTES per GPU (route.hip) whose counter head is cleared on
+// the stream before the launch.  Needs route_workspace_bytes(T, H, E, dtype)
+// <= ROUTE_SCRATCH_BYTES (checked by the caller).  Returns 0, or 1 when the
+// array's device address could not be found (nothing was enqueued).
+constexpr size_t ROUTE_SCRATCH_BYTES = size_t(16) << 20;
+int launch_route_permute_scratch(int dtype, const void* x, const void* wg, const float* bias, float* logits,
+                                 int32_t* ids, float* w, int T, int H, int E, int k, int renorm,
+                                 int n_shared, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,
+                                 int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s);
 void launch_route(int dtype, const void* x, const void* wg, const float* bias, float* logits,
                   int32_t* ids, float* w, int T, int H, int E, int k, int renorm, int n_shared,
                   void* ws, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,

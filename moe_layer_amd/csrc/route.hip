@@ -38,6 +38,8 @@
 // instead write back and invalidate the whole L2 of every arriving block.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "moe_internal.h"
 #include "sort.hpp"
@@ -407,6 +409,71 @@ static void launch_route_t(const RoutePlan& p, const RouteArgs& a, hipStream_t s
     case 8: hipLaunchKernelGGL((route_kernel<T, 8>), grid, block, 0, s, a); break;
     default: hipLaunchKernelGGL((route_kernel<T, 16>), grid, block, 0, s, a); break;
   }
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+//
+// A fixed scratch region in device memory for callers that cannot allocate a
+// workspace.  It is a file-scope device array: every GPU the library runs on
+// holds its own copy, at its own address, until the process ends.  On the
+// host its name is only a stand-in for that address, so host code never
+// passes it to a kernel; it uses the per-device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current.  All calls on one GPU share its copy (calls that overlap in time
+// race on it).
+static __device__ __align__(256) char scratch[ROUTE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[SCRATCH_MAX_DEVICES];
+
+// The current device's copy of `scratch`, or nullptr with *err set.
+void* scratch_address(hipError_t* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    void* p = nullptr;
+    slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (slot.err == hipSuccess && p == nullptr) slot.err = hipErrorInvalidSymbol;
+    slot.ptr = slot.err == hipSuccess ? p : nullptr;
+  });
+  *err = slot.err;
+  return slot.ptr;
+}
+
+__global__ void zero_ints_kernel(int* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+}  // namespace
+
+int launch_route_permute_scratch(int dtype, const void* x, const void* wg, const float* bias, float* logits,
+                                 int32_t* ids, float* w, int T, int H, int E, int k, int renorm,
+                                 int n_shared, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,
+                                 int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s) {
+  hipError_t err = hipSuccess;
+  void* ptr = scratch_address(&err);
+  if (ptr == nullptr) return 1;
+  // The counters must start at zero: a fill kernel (not a memset node, so
+  // the call stays capturable in a graph) clears them on the stream first.
+  const RoutePlan p = plan_route(T, H, E, dtype);
+  const int n_ctr = p.n_tt + 1;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((n_ctr + 255) / 256), dim3(256), 0, s, static_cast<int*>(ptr), n_ctr);
+  launch_route(dtype, x, wg, bias, logits, ids, w, T, H, E, k, renorm, n_shared, ptr, g_begin, n_groups, counts,
+               offsets, sorted_pair, pair_pos, s);
+  return 0;
 }
 
 void launch_route(int dtype, const void* x, const void* wg, const float* bias, float* logits,

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 7
+    assert L.moe_abi_version() == 8
     for s in range(5):
         assert L.moe_status_str(s).decode().startswith(
             ["MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP"][s])
@@ -114,6 +114,25 @@ def test_route_rejects(L, kw, status):
 ])
 def test_route_permute_rejects(L, kw, status):
     assert route_permute(L, **kw) == status
+
+
+def route_permute_noalloc(L, T=4, H=256, E=8, k=2, g_begin=0, n_groups=8, counts=FAKE, x=FAKE):
+    return L.moe_route_permute_noalloc(x, FAKE, None, T, H, E, k, 1, 0, BF16, FAKE, FAKE, FAKE, g_begin,
+                                       n_groups, counts, FAKE, FAKE, FAKE, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g_begin=-1), MOE_EINVAL),
+    (dict(n_groups=513), MOE_EUNSUPPORTED),
+    (dict(counts=None), MOE_EINVAL),
+    (dict(x=None), MOE_EINVAL),
+    (dict(k=9), MOE_EINVAL),
+    (dict(E=513), MOE_EUNSUPPORTED),
+    # 2^22 + 1 token-tile counters need more than the 16 MiB fixed scratch
+    (dict(T=1 << 26, k=8), MOE_EWORKSPACE),
+])
+def test_route_permute_noalloc_rejects(L, kw, status):
+    assert route_permute_noalloc(L, **kw) == status
 
 
 def test_route_workspace_size(L):
