@@ -368,7 +368,8 @@ def parse():
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("expert_gemm.hip", "expert_tile.hip", "common.hpp", "moe_internal.h"):
+    for f in ("expert_gemm.hip", "expert_coop.hip", "expert_tile.hip", "stream_ops.hpp", "common.hpp",
+              "moe_internal.h"):
         with open(os.path.join(ROOT, "moe_layer_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -585,8 +586,8 @@ def ingest_counters(fetch_csv, write_csv, name, T, routing, command):
         with open(path) as f:
             for row in csv.DictReader(f):
                 kname = row.get("Kernel_Name", "")
-                if "expert_wave_kernel" not in kname or ", 0, " not in kname:
-                    continue   # the up-projection is expert_wave_kernel<T, 0, ...>
+                if not ("expert_wave_kernel" in kname or "expert_coop_kernel" in kname) or ", 0, " not in kname:
+                    continue   # the up-projection: expert_{wave,coop}_kernel<T, 0, ...>
                 if row.get("Counter_Name") != counter:
                     continue
                 vals.setdefault(row.get("Dispatch_Id"), 0.0)
@@ -601,7 +602,7 @@ def ingest_counters(fetch_csv, write_csv, name, T, routing, command):
     c.setdefault("fetch_scale", 1.9994)
     c.setdefault("write_scale", 0.9997)
     entries = [e for e in c.get("entries", []) if (e.get("workload"), e.get("T"), e.get("routing")) != (name, T, routing)]
-    entries.append({"workload": name, "T": T, "routing": routing, "kernel": "moe_expert_up (expert_wave_kernel<bf16, UP, ...>)",
+    entries.append({"workload": name, "T": T, "routing": routing, "kernel": "moe_expert_up (expert_{wave,coop}_kernel<bf16, UP, ...>)",
                     "source_sha": kernel_source_sha(), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
                     "dispatches": min(nf, nw), "commands": command})
     c["entries"] = sorted(entries, key=lambda e: (e["workload"], e["routing"], e["T"]))
