@@ -45,7 +45,10 @@ void launch_route(int dtype, const void* x, const void* wg, const float* bias, f
                   int32_t* ids, float* w, int T, int H, int E, int k, int renorm, int n_shared,
                   void* ws, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,
                   int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s);
-// counts, offsets, stable permutation
+// counts, offsets, stable permutation: one block up to PERM_ONE_BLOCK_MAX
+// pairs, above that one block per segment of pairs (permute_uses_blocks)
+constexpr long long PERM_ONE_BLOCK_MAX = 4096;
+bool permute_uses_blocks(int T, int kk);
 void launch_permute(const int32_t* ids, int T, int kk, int g_begin, int n_groups, int32_t* counts,
                     int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s);
 // EP dispatch: pairs by owning rank ids / E_local (< P), then the send rows

@@ -244,17 +244,33 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
                      static_cast<size_t>(min(et * 16 + lrow, a.E - 1)) * row_bytes + lq * 16;
     const char* xp = reinterpret_cast<const char*>(a.x) +
                      static_cast<size_t>(min(tt * 16 + lrow, a.T - 1)) * row_bytes + lq * 16;
+    // Two register buffers of RT_CHUNK fragments: the next chunk's loads are
+    // in flight while the current one is multiplied.  Addresses are clamped
+    // into the slice, so every load is unconditional; fragments past the
+    // slice end meet zero token fragments.
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int f0 = f_begin; f0 < f_end; f0 += RT_CHUNK) {
-      uint4 wf[RT_CHUNK], xf[RT_CHUNK];
+    if (f_begin < f_end) {
+      uint4 wa[RT_CHUNK], xa[RT_CHUNK], wb[RT_CHUNK], xb[RT_CHUNK];
+      auto load = [&](int f0, uint4 (&wf)[RT_CHUNK], uint4 (&xf)[RT_CHUNK]) {
 #pragma unroll
-      for (int i = 0; i < RT_CHUNK; ++i) {
-        const int f = min(f0 + i, f_end - 1);
-        wf[i] = ld16(wp + f * FRAG_BYTES);
-        xf[i] = ld16(xp + f * FRAG_BYTES);
+        for (int i = 0; i < RT_CHUNK; ++i) {
+          const int f = min(f0 + i, f_end - 1);
+          wf[i] = ld16(wp + f * FRAG_BYTES);
+          xf[i] = ld16(xp + f * FRAG_BYTES);
+        }
+      };
+      auto mma = [&](int f0, const uint4 (&wf)[RT_CHUNK], const uint4 (&xf)[RT_CHUNK]) {
+#pragma unroll
+        for (int i = 0; i < RT_CHUNK; ++i) acc = Elem<T>::mma(wf[i], keep_or_zero(f0 + i < f_end, xf[i]), acc);
+      };
+      load(f_begin, wa, xa);
+      for (int f0 = f_begin; f0 < f_end; f0 += 2 * RT_CHUNK) {
+        load(f0 + RT_CHUNK, wb, xb);
+        mma(f0, wa, xa);
+        if (f0 + RT_CHUNK >= f_end) break;
+        load(f0 + 2 * RT_CHUNK, wa, xa);
+        mma(f0 + RT_CHUNK, wb, xb);
       }
-#pragma unroll
-      for (int i = 0; i < RT_CHUNK; ++i) acc = Elem<T>::mma(wf[i], keep_or_zero(f0 + i < f_end, xf[i]), acc);
     }
     // acc[r] = D[4*lq + r][lrow]: expert et*16 + 4*lq + r, token tt*16 + lrow.
     const int t = tt * 16 + lrow;
@@ -480,6 +496,14 @@ void launch_route(int dtype, const void* x, const void* wg, const float* bias, f
                   int32_t* ids, float* w, int T, int H, int E, int k, int renorm, int n_shared,
                   void* ws, int g_begin, int n_groups, int32_t* counts, int32_t* offsets,
                   int32_t* sorted_pair, int32_t* pair_pos, hipStream_t s) {
+  // Many pairs: one block sorting them all would set the launch's end, so the
+  // routing launch stops after the top-k and the multi-block permute follows.
+  if (counts != nullptr && permute_uses_blocks(T, k + n_shared)) {
+    launch_route(dtype, x, wg, bias, logits, ids, w, T, H, E, k, renorm, n_shared, ws, g_begin, n_groups,
+                 nullptr, nullptr, nullptr, nullptr, s);
+    launch_permute(ids, T, k + n_shared, g_begin, n_groups, counts, offsets, sorted_pair, pair_pos, s);
+    return;
+  }
   const RoutePlan p = plan_route(T, H, E, dtype);
   RouteArgs a{};
   a.x = x;

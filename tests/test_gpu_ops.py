@@ -182,8 +182,15 @@ def test_permute_arbitrary_ids():
     import gpu_helpers as gh
     import moe_layer_amd
     rng = np.random.default_rng(11)
-    for T, kk, g_begin, n_groups in [(1000, 7, 5, 40), (3, 1, 0, 1), (2048, 8, 0, 130), (64, 64, 100, 7)]:
+    # One block sorts up to 4096 pairs; above that one block per 1024-pair
+    # segment (the first cases): ragged last segments, 512 groups, a window
+    # holding none of the ids, and the 4096 / 4097 boundary.
+    for T, kk, g_begin, n_groups in [(1000, 7, 5, 40), (3, 1, 0, 1), (2048, 8, 0, 130), (64, 64, 100, 7),
+                                     (4097, 1, 0, 512), (4096, 1, 0, 512), (700, 8, 3, 509),
+                                     (20000, 3, 0, 16), (3000, 2, 900, 5)]:
         ids = rng.integers(-3, g_begin + n_groups + 5, size=(T, kk)).astype(np.int32)
+        if g_begin == 900:
+            ids = rng.integers(0, 800, size=(T, kk)).astype(np.int32)   # nothing in the window
         print(f"[case] permute T={T} kk={kk} window=({g_begin},{n_groups})", flush=True)
         dev = gh.to_dev(ids)
         out = [torch.empty(s, dtype=torch.int32, device="cuda") for s in
