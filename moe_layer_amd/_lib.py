@@ -12,7 +12,9 @@ import os
 import torch  # noqa: F401  (must load first: the library shares torch's HIP runtime)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_layer_amd.so")
+# The in-tree build; MOE_LAYER_AMD_LIB names another build of the same
+# sources (e.g. the host-sanitized one of build_sanitized.py).
+LIB_PATH = os.environ.get("MOE_LAYER_AMD_LIB") or os.path.join(HERE, "libmoe_layer_amd.so")
 
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
