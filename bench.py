@@ -486,8 +486,8 @@ def time_workload(wl, steps, warmup, graph=False):
     calls in the loop: an event record is a queue packet of its own and costs
     the GPU ~5 us of idle time, so events would inflate the step.  Then
     MEDIAN_BLOCKS - 1 more blocks of K steps (the median of the block means
-    is ms_per_step_median).  A further pass of K steps records two HIP events
-    per step on the launch stream around the up-projection: their mean is the
+    is ms_per_step_median).  Then K up-projection launches back to back on
+    the last step's routing between two HIP events on the launch stream: the
     dominant kernel's duration.  A last pass with events around every call
     gives the other kernels' durations (those include the event packets).
     With graph=True the step is also captured in HIP graphs (one per weight
@@ -504,13 +504,19 @@ def time_workload(wl, steps, warmup, graph=False):
         torch.cuda.synchronize()
         blocks.append((time.perf_counter() - t0) / steps)
     t_step = blocks[0]          # the K timed steps
-    up = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    # The up-projection's own duration: K launches back to back (on the last
+    # step's routing, weight copies rotated) between two events on the launch
+    # stream, so no event packet sits between launches.
+    import moe_layer_amd as m
+    c, b = wl.cfg, wl.bufs
+    e_up0, e_up1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    e_up0.record()
     for i in range(steps):
-        run_step(wl, i, up_events=up[i])
+        m.moe_expert_up(wl.x, b.sorted_pair, b.offsets, c.kk, wl.w13[i % wl.copies], b.a, b.expert_ws)
+    e_up1.record()
     torch.cuda.synchronize()
-    t_up_us = sum(a.elapsed_time(b) for a, b in up) / steps * 1e3
+    t_up_us = e_up0.elapsed_time(e_up1) / steps * 1e3
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
