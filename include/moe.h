@@ -108,10 +108,11 @@ int moe_route(const void* x, const void* w_gate, const float* gate_bias, int T, 
               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * moe_route_permute -- moe_route followed by moe_permute of its ids, in one
- * launch (the last block to finish the routing sorts the pairs).  Arguments
- * and outputs are those of the two calls; the same workspace rules as
- * moe_route apply.
+ * moe_route_permute -- moe_route followed by moe_permute of its ids.  Up to
+ * 4096 pairs (T*(k+n_shared)) this is one launch: the last block to finish
+ * the routing sorts the pairs.  Above that the routing launch is followed by
+ * moe_permute's own launches on the same stream.  Arguments and outputs are
+ * those of the two calls; the same workspace rules as moe_route apply.
  */
 int moe_route_permute(const void* x, const void* w_gate, const float* gate_bias, int T, int H, int E,
                       int k, int renorm, int n_shared, int dtype, float* logits, int32_t* topk_ids,
@@ -156,6 +157,10 @@ int moe_route_permute_noalloc(const void* x, const void* w_gate, const float* ga
  * Views: full / TP: g_begin = 0, n_groups = E + n_shared; EP rank r with
  * E_l = E/P local experts: g_begin = r*E_l, n_groups = E_l.
  * Limits: 1 <= kk <= 64; 1 <= n_groups <= 512.  Results are deterministic.
+ * Above 65536 pairs the sort takes three launches and parks per-segment
+ * group counts in pair_pos between them, so no output may overlap topk_ids
+ * (true of every size) and pair_pos holds its final values only once the
+ * call's work on `stream` has completed.
  */
 int moe_permute(const int32_t* topk_ids, int T, int kk, int g_begin, int n_groups, int32_t* counts,
                 int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t stream);

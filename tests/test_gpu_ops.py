@@ -203,6 +203,64 @@ def test_permute_arbitrary_ids():
         assert np.array_equal(got[2][:o[-1]], sp) and np.array_equal(got[3], pos)
 
 
+def stable_sort_properties(ids, g_begin, n_groups, counts, offsets, sorted_pair, pair_pos):
+    """What fixes a stable counting sort at any size, checked with vector ops:
+    the counts are the histogram, the offsets its exclusive sum, sorted_pair
+    lists every held pair once, in group order and ascending inside a group,
+    and pair_pos is its inverse (-1 for pairs not held)."""
+    key = ids.ravel().astype(np.int64) - g_begin
+    held = (key >= 0) & (key < n_groups)
+    hist = np.bincount(key[held], minlength=n_groups)
+    assert np.array_equal(counts, hist)
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets.astype(np.int64)), hist)
+    n_kept = int(offsets[-1])
+    sp = sorted_pair[:n_kept].astype(np.int64)
+    assert np.array_equal(np.sort(sp), np.flatnonzero(held))
+    g_of_row = key[sp]
+    assert (np.diff(g_of_row) >= 0).all()
+    same = np.diff(g_of_row) == 0
+    assert (np.diff(sp)[same] > 0).all()
+    expect_pos = np.full(key.size, -1, dtype=np.int64)
+    expect_pos[sp] = np.arange(n_kept)
+    assert np.array_equal(pair_pos, expect_pos)
+
+
+def test_permute_large_tables():
+    import torch
+
+    import gpu_helpers as gh
+    import moe_layer_amd
+    rng = np.random.default_rng(12)
+    # Above 65536 pairs the sort runs as count / column-scan / scatter launches
+    # with per-segment counts parked in pair_pos: both sides of the line, a
+    # ragged last segment, every pair in one group, an empty window, 2048
+    # segments of 1024 pairs and 2048 segments of 4096 pairs.
+    cases = [(65536, 1, 0, 512, True), (65537, 1, 0, 512, True), (40000, 8, 0, 128, True),
+             (70000, 2, 0, 3, True), (80000, 1, 900, 5, True), (262144, 8, 64, 16, False),
+             (1 << 20, 8, 0, 512, False)]
+    for T, kk, g_begin, n_groups, use_oracle in cases:
+        if g_begin == 900:
+            ids = rng.integers(0, 800, size=(T, kk)).astype(np.int32)
+        elif n_groups == 3:
+            ids = np.where(rng.random((T, kk)) < 0.97, 1, rng.integers(-1, 4, size=(T, kk))).astype(np.int32)
+        else:
+            ids = rng.integers(-3, g_begin + n_groups + 5, size=(T, kk)).astype(np.int32)
+        print(f"[case] permute large T={T} kk={kk} window=({g_begin},{n_groups})", flush=True)
+        dev = gh.to_dev(ids)
+        out = [torch.full((s,), -7, dtype=torch.int32, device="cuda") for s in
+               (n_groups, n_groups + 1, T * kk, T * kk)]
+        moe_layer_amd.moe_permute(dev, g_begin, n_groups, *out)
+        torch.cuda.synchronize()
+        got = [gh.from_dev(t) for t in out]
+        if use_oracle:
+            c, o, sp, pos = oracle.permute(ids, g_begin, n_groups)
+            assert np.array_equal(got[0], c) and np.array_equal(got[1], o)
+            assert np.array_equal(got[2][:o[-1]], sp) and np.array_equal(got[3], pos)
+        else:
+            stable_sort_properties(ids, g_begin, n_groups, *got)
+        del dev, out
+
+
 def test_permute_empty_batch_writes_zero_counts():
     import torch
 
@@ -347,10 +405,11 @@ def test_graph_replay_matches_eager():
 @pytest.mark.parametrize("T,E,k,n_shared,H", [(3000, 64, 8, 0, 256), (8, 128, 8, 0, 4096),
                                                (40, 64, 6, 2, 2048), (1, 128, 8, 0, 4096),
                                                (13, 128, 8, 2, 4096), (16, 64, 6, 2, 2048),
-                                               (17, 128, 8, 0, 4096)])
+                                               (17, 128, 8, 0, 4096), (9000, 64, 8, 0, 256)])
 def test_fused_route_matches_two_calls_and_leaves_workspace_zero(T, E, k, n_shared, H):
     """One launch (routing + sort) against moe_route then moe_permute; the
-    3000-token case has more pairs than the sort stages in LDS.  At H = 2048
+    3000-token case has more pairs than the sort stages in LDS, and 9000
+    tokens (72 000 pairs) route and then sort in the three-launch permute.  At H = 2048
     and 4096 the gate GEMM runs 8 or 16 K slices summed per block; T <= 16
     (one token tile, T = 1 and 13 ragged) sorts in the top-k block from LDS,
     and T = 17 hands a one-token second tile to the sorting block."""
