@@ -10,7 +10,9 @@
 // weight 1 copies its row exactly (signed zeros included).
 //
 // Each thread owns one 16-byte vector of one token row; the slot positions and
-// weights of that token are block-uniform.
+// weights of that token are block-uniform (scalar loads).  Slots are taken
+// eight at a time: their positions first, then all eight row loads, then the
+// sums in slot order, so a token's rows arrive in one round trip.
 #include "common.hpp"
 #include "moe_internal.h"
 
@@ -27,22 +29,36 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const T* __res
   const int t = blockIdx.x / h_blocks;
   const int h0 = ((blockIdx.x % h_blocks) * COMBINE_THREADS + threadIdx.x) * VEC;
   if (h0 >= H) return;
+  constexpr int SLOTS = 8;
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
   bool first = true;
-  for (int j = 0; j < kk; ++j) {
-    const int pos = pair_pos[static_cast<size_t>(t) * kk + j];
-    if (pos < 0) continue;
-    const float wj = w ? w[static_cast<size_t>(t) * kk + j] : 1.f;
-    const uint4 v = ld16(y_pair + static_cast<size_t>(pos) * H + h0);
-    const T* e = reinterpret_cast<const T*>(&v);
+  const int32_t* pp = pair_pos + static_cast<size_t>(t) * kk;
+  const float* pw = w ? w + static_cast<size_t>(t) * kk : nullptr;
+  for (int j0 = 0; j0 < kk; j0 += SLOTS) {
+    int pos[SLOTS];
+    float wj[SLOTS];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      const float term = wj * Elem<T>::load(e + i);
-      acc[i] = first ? term : acc[i] + term;
+    for (int u = 0; u < SLOTS; ++u) {
+      pos[u] = j0 + u < kk ? pp[j0 + u] : -1;
+      wj[u] = (pw && j0 + u < kk) ? pw[j0 + u] : 1.f;
     }
-    first = false;
+    uint4 v[SLOTS];
+#pragma unroll
+    for (int u = 0; u < SLOTS; ++u)
+      v[u] = pos[u] >= 0 ? ld16(y_pair + static_cast<size_t>(pos[u]) * H + h0) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < SLOTS; ++u) {
+      if (pos[u] < 0) continue;
+      const T* e = reinterpret_cast<const T*>(&v[u]);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const float term = wj[u] * Elem<T>::load(e + i);
+        acc[i] = first ? term : acc[i] + term;
+      }
+      first = false;
+    }
   }
   T* dst = y + static_cast<size_t>(t) * H + h0;
 #pragma unroll

@@ -11,7 +11,7 @@ namespace moe {
 
 // Limits shared by the host checks and the kernels.
 constexpr int MAX_GROUPS = 512;   // expert groups per call (LDS tables)
-constexpr int MAX_E = 512;        // routed experts in the gate (8 logits per lane)
+constexpr int MAX_E = 512;        // routed experts in the gate (16 logits per top-k lane)
 constexpr int MAX_K = 32;         // routed picks per token
 constexpr int MAX_KK = 64;        // routed + shared slots per token
 constexpr int MAX_P = 64;         // peers in a repack

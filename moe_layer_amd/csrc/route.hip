@@ -16,11 +16,12 @@
 // Phase B -- the block that completes a token tile's counter (the last one to
 //   arrive; integer atomics, nobody waits) sums the KS partials of each of
 //   the tile's logits in slice order, adds the bias and writes the logits
-//   (to HBM and to LDS), then runs the top-k of each token, one wave per
-//   token: lane l holds experts l, l+64, ...; each of the k rounds reduces
-//   (value, id) over the wave with a xor-butterfly under "larger value
-//   first, then lower id" -- a total order, so every lane sees the same
-//   winner and equal logits (-0.0 vs +0.0 included) go to the lower id.
+//   (to HBM and to LDS), then runs the top-k of each token, 32 lanes per
+//   token: lane l holds experts l, l+32, ...; each of the k rounds reduces
+//   the largest logit key over the lanes, then the lowest expert id holding
+//   it -- "larger value first, then lower id", a total order, so every lane
+//   sees the same winner and equal logits (-0.0 vs +0.0 included) go to the
+//   lower id.
 //   Selection is on the fp32 logits (the same set as on the softmax).
 //   Weights: softmax over all E routed experts at the picks, optionally
 //   renormalised over the k picks; shared experts E, E+1, ... follow with
@@ -77,71 +78,82 @@ struct RouteArgs {
   int bpt;                 // blocks per token tile
 };
 
-// Top-k of one token by a group of 16 lanes (4 tokens per wave): lane r of
-// the group holds experts r, r+16, r+32, ... as 64-bit keys
-//   (order-preserving image of the fp32 logit) << 32 | (2^32 - 1 - expert)
-// so that one unsigned max picks the larger logit and, among equal logits
-// (-0.0 and +0.0 included), the lower expert id.  Each of the k rounds takes
-// the lane maxima, reduces them over the group with DPP moves (quad xor 1,
-// quad xor 2, half-row mirror, row mirror: every lane ends with the same
-// winner) and clears the winner's key.  Selection is on the fp32 logits,
-// the same set as on the softmax.
-constexpr int TK_LANES = 16;
+// Top-k of one token by a group of 32 lanes (2 tokens per wave, 16 per block):
+// lane r of the group holds experts r, r+32, r+64, ... as 32-bit keys, the
+// order-preserving image of the fp32 logit (-0.0 and +0.0 map to one key; 0
+// marks an empty or taken slot, so real keys are at least 1).  Each of the k
+// rounds takes the lane maxima and reduces them over the group (DPP quad xor
+// 1, quad xor 2, half-row mirror, row mirror, then the two 16-lane rows
+// combined with v_permlane16_swap: every lane ends with the same value);
+// among the experts holding that key the lowest id wins (a second, min
+// reduction of ids), so equal logits go to the lower expert id.  Selection is
+// on the fp32 logits, the same set as on the softmax.
+constexpr int TK_LANES = 32;
 constexpr int TK_MAXV = MAX_E / TK_LANES;
 
-__device__ __forceinline__ uint64_t logit_key(float v, int e) {
+__device__ __forceinline__ uint32_t logit_key(float v) {
   uint32_t u = __float_as_uint(v);
   if (u == 0x80000000u) u = 0u;  // -0.0 ties with +0.0
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (static_cast<uint64_t>(u) << 32) | (0xffffffffu - static_cast<uint32_t>(e));
+  return u > 1u ? u : 1u;        // only a negative NaN maps below 1
 }
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  const uint32_t u = static_cast<uint32_t>(key >> 32);
+__device__ __forceinline__ float key_logit(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
-}
-__device__ __forceinline__ int key_expert(uint64_t key) {
-  return static_cast<int>(0xffffffffu - static_cast<uint32_t>(key));
 }
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp32(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xf, 0xf, false));
 }
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
-  const uint64_t o = (static_cast<uint64_t>(dpp32<CTRL>(static_cast<uint32_t>(v >> 32))) << 32) |
-                     dpp32<CTRL>(static_cast<uint32_t>(v));
-  return o > v ? o : v;
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-  return v + __uint_as_float(dpp32<CTRL>(__float_as_uint(v)));
+// The values of lanes i & ~16 and i | 16 (the two 16-lane rows of lane i's
+// 32-lane half), in that order in every lane: v_permlane16_swap of a
+// register with itself.
+struct RowPair {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ RowPair row_pair(uint32_t v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return RowPair{p[0], p[1]};
 }
 constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7 - i within 8
 constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15 - i within 16
 
-__device__ __forceinline__ uint64_t group16_max(uint64_t v) {
-  v = dpp_max<DPP_XOR1>(v);
-  v = dpp_max<DPP_XOR2>(v);
-  v = dpp_max<DPP_HALF_MIRROR>(v);
-  return dpp_max<DPP_MIRROR>(v);
+__device__ __forceinline__ uint32_t group32_max(uint32_t v) {
+  v = max(v, dpp32<DPP_XOR1>(v));
+  v = max(v, dpp32<DPP_XOR2>(v));
+  v = max(v, dpp32<DPP_HALF_MIRROR>(v));
+  v = max(v, dpp32<DPP_MIRROR>(v));
+  const RowPair p = row_pair(v);
+  return max(p.lo, p.hi);
 }
-// Every lane of the group gets the same bits: each level adds two equal
-// partial sums in either order, and fp32 addition is commutative.
-__device__ __forceinline__ float group16_sum(float v) {
-  v = dpp_add<DPP_XOR1>(v);
-  v = dpp_add<DPP_XOR2>(v);
-  v = dpp_add<DPP_HALF_MIRROR>(v);
-  return dpp_add<DPP_MIRROR>(v);
+__device__ __forceinline__ uint32_t group32_min(uint32_t v) {
+  v = min(v, dpp32<DPP_XOR1>(v));
+  v = min(v, dpp32<DPP_XOR2>(v));
+  v = min(v, dpp32<DPP_HALF_MIRROR>(v));
+  v = min(v, dpp32<DPP_MIRROR>(v));
+  const RowPair p = row_pair(v);
+  return min(p.lo, p.hi);
+}
+// Every lane of the group gets the same bits: each DPP level adds two equal
+// partial sums in either order (fp32 addition is commutative), and the last
+// adds the two rows' sums in the same order in every lane.
+__device__ __forceinline__ float group32_sum(float v) {
+  v += __uint_as_float(dpp32<DPP_XOR1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp32<DPP_XOR2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp32<DPP_HALF_MIRROR>(__float_as_uint(v)));
+  v += __uint_as_float(dpp32<DPP_MIRROR>(__float_as_uint(v)));
+  const RowPair p = row_pair(__float_as_uint(v));
+  return __uint_as_float(p.lo) + __uint_as_float(p.hi);
 }
 
-// lg: the token's E logits (LDS), E <= 16 * V.  All 16 lanes of the group
+// lg: the token's E logits (LDS), E <= 32 * V.  All 32 lanes of the group
 // call this.  Weights: softmax over all E routed experts at the picks,
-// optionally renormalised over the k picks; shared experts E, E+1, ...
-// follow with weight 1.  pk (LDS, nullable): the sort keys of the token's
-// k + n_shared pairs (expert - g_begin when in [0, n_groups), else n_groups).
+// optionally renormalised over the k picks (the sum over all E then cancels
+// and is not formed); shared experts E, E+1, ... follow with weight 1.  pk
+// (LDS, nullable): the sort keys of the token's k + n_shared pairs (expert -
+// g_begin when in [0, n_groups), else n_groups).
 __device__ __forceinline__ uint16_t local_key(int id, int g_begin, int n_groups) {
   const int g = id - g_begin;
   return static_cast<uint16_t>((g >= 0 && g < n_groups) ? g : n_groups);
@@ -151,48 +163,49 @@ __device__ __forceinline__ void group_topk(const float* lg, int E, int k, int re
                                            int32_t* ids, float* w, uint16_t* pk, int g_begin,
                                            int n_groups) {
   const int r = lane_id() & (TK_LANES - 1);
-  uint64_t key[V];  // key 0 never wins: every real key is larger
+  uint32_t key[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const int e = r + TK_LANES * j;
-    key[j] = e < E ? logit_key(lg[e], e) : 0ull;
+    key[j] = e < E ? logit_key(lg[e]) : 0u;
   }
-  uint64_t pick0 = 0, pick1 = 0;  // this lane's picks: rounds r and r + 16
+  uint32_t pick = 0, top = 0;   // this lane's pick: round r; the first round's key
+  int pick_id = 0;
   for (int round = 0; round < k; ++round) {
-    uint64_t best = 0;
+    uint32_t m = key[0];
 #pragma unroll
-    for (int j = 0; j < V; ++j) best = key[j] > best ? key[j] : best;
-    best = group16_max(best);
+    for (int j = 1; j < V; ++j) m = max(m, key[j]);
+    const uint32_t best = group32_max(m);
+    uint32_t cand = 0xffffffffu;  // this lane's lowest expert holding `best`
 #pragma unroll
-    for (int j = 0; j < V; ++j) key[j] = key[j] == best ? 0ull : key[j];
-    if (r == (round & (TK_LANES - 1))) {
-      if (round < TK_LANES) pick0 = best;
-      else pick1 = best;
+    for (int j = V - 1; j >= 0; --j) cand = key[j] == best ? static_cast<uint32_t>(r + TK_LANES * j) : cand;
+    const uint32_t win = group32_min(cand);
+#pragma unroll
+    for (int j = 0; j < V; ++j) key[j] = static_cast<uint32_t>(r + TK_LANES * j) == win ? 0u : key[j];
+    if (round == 0) top = best;
+    if (r == round) {
+      pick = best;
+      pick_id = static_cast<int>(win);
     }
   }
-  // max logit = the first pick, held by lane 0 of the group
-  const float mx = key_logit(static_cast<uint64_t>(__shfl(static_cast<long long>(pick0),
-                                                          lane_id() & ~(TK_LANES - 1), WAVE)));
-  float s_all = 0.f;
+  const float mx = key_logit(top);  // the largest logit
+  const float p = (r < k) ? expf(key_logit(pick) - mx) : 0.f;
+  float denom;
+  if (renorm) {
+    denom = group32_sum(p);
+  } else {
+    float s_all = 0.f;
 #pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int e = r + TK_LANES * j;
-    if (e < E) s_all += expf(lg[e] - mx);
+    for (int j = 0; j < V; ++j) {
+      const int e = r + TK_LANES * j;
+      if (e < E) s_all += expf(lg[e] - mx);
+    }
+    denom = group32_sum(s_all);
   }
-  const float p0 = (r < k) ? expf(key_logit(pick0) - mx) : 0.f;
-  const float p1 = (r + TK_LANES < k) ? expf(key_logit(pick1) - mx) : 0.f;
-  s_all = group16_sum(s_all);
-  const float s_sel = group16_sum(p0 + p1);
-  const float denom = renorm ? s_sel : s_all;
   if (r < k) {
-    st_agent(ids + r, key_expert(pick0));
-    w[r] = p0 / denom;
-    if (pk) pk[r] = local_key(key_expert(pick0), g_begin, n_groups);
-  }
-  if (r + TK_LANES < k) {
-    st_agent(ids + r + TK_LANES, key_expert(pick1));
-    w[r + TK_LANES] = p1 / denom;
-    if (pk) pk[r + TK_LANES] = local_key(key_expert(pick1), g_begin, n_groups);
+    st_agent(ids + r, pick_id);
+    w[r] = p / denom;
+    if (pk) pk[r] = local_key(pick_id, g_begin, n_groups);
   }
   for (int sh = r; sh < n_shared; sh += TK_LANES) {
     st_agent(ids + k + sh, E + sh);
@@ -336,7 +349,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  // ---------------- phase B2: top-k of the tile's tokens, 16 lanes per token
+  // ---------------- phase B2: top-k of the tile's tokens, 32 lanes per token
   const int kk = a.k + a.n_shared;
   // A single token tile sorts in this block: its pair keys stay in LDS.
   const bool one_tile = a.n_tt == 1 && a.counts != nullptr;
@@ -348,9 +361,9 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
       int32_t* ids = a.ids + t * kk;
       float* w = a.w + t * kk;
       uint16_t* pk = one_tile ? s_pk + j * kk : nullptr;
-      if (a.E <= 4 * TK_LANES) group_topk<4>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w, pk, a.g_begin, a.n_groups);
+      if (a.E <= 2 * TK_LANES) group_topk<2>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w, pk, a.g_begin, a.n_groups);
+      else if (a.E <= 4 * TK_LANES) group_topk<4>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w, pk, a.g_begin, a.n_groups);
       else if (a.E <= 8 * TK_LANES) group_topk<8>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w, pk, a.g_begin, a.n_groups);
-      else if (a.E <= 16 * TK_LANES) group_topk<16>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w, pk, a.g_begin, a.n_groups);
       else group_topk<TK_MAXV>(lg, a.E, a.k, a.renorm, a.n_shared, ids, w, pk, a.g_begin, a.n_groups);
     }
   }
