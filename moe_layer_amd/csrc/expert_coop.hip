@@ -7,8 +7,8 @@
 // (Moebius review, §3.1: W13 (., 2I, H); decode MoE GEMMs are memory-bound,
 // §2.1 and Fig. 3, so every weight byte must stream once.)
 //
-// Work item = (group, `sub` adjacent 16-row weight tiles, pass of up to 32
-// token rows) over the full K, as in expert_gemm.hip.  An item is cut into
+// Work item = (group, `sub` adjacent 16-row weight tiles, pass of 16 token
+// rows) over the full K, as in expert_gemm.hip.  An item is cut into
 // units of one tile x one 512-byte chunk of K (16 rows x 512 B = 8 KB of
 // weights), at most CO_UNITS_MAX per item; units are numbered tile-major, so
 // the waves working on an item at the same time read neighbouring bytes of the
