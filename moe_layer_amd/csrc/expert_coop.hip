@@ -113,7 +113,8 @@ __device__ __forceinline__ void co_store(const XArgs& a, const WItem<CO_NT>& it,
 // [t0, m_end), the first weight row n0 of its tiles, the tiles inside the
 // matrix, and the weight row its first tile starts at.  Wave-uniform.
 struct CoItem {
-  int tag, row0, m_end, t0, n0, n_sub, first_row, pad;
+  int tag, row0, m_end, t0, n0, n_sub, first_row;
+  int pad;   // 1 when the item's tile has later passes (the weights are kept in L2)
 };
 
 template <int MODE>
@@ -126,11 +127,11 @@ __device__ __forceinline__ CoItem co_decode(const XArgs& a, const int* s_istart,
   }
   CoItem d;
   d.tag = item;
-  d.pad = 0;
   d.row0 = uni(s_off[lo]);
   const int m = uni(s_off[lo + 1]) - d.row0;
   const int ps = pass_rows<CO_NT>(m);
   const int np = (m + ps - 1) / ps;
+  d.pad = np > 1 ? 1 : 0;   // the tile has later passes
   const int local = item - uni(s_istart[lo]);
   const int nq = local / np;
   d.t0 = (local - nq * np) * ps;
@@ -156,18 +157,36 @@ __device__ __forceinline__ int co_token_row(const XArgs& a, const CoItem& d, int
 
 }  // namespace
 
-template <typename T, int MODE, bool FULLK>
-__global__ __launch_bounds__(CO_THREADS) void expert_coop_kernel(XArgs a) {
-  __shared__ int s_istart[MAX_GROUPS + 1];
-  __shared__ int s_off[MAX_GROUPS + 1];
-  __shared__ int s_ntx;
-  __shared__ int s_next, s_maxm;
-  __shared__ int s_done[CO_RING_MAX], s_fin[CO_RING_MAX];
-  __shared__ __attribute__((aligned(16))) CoItem s_info[CO_INFO];
-  __shared__ int s_tok[CO_INFO][16 * CO_NT];
-  __shared__ __attribute__((aligned(16))) char s_wt[CO_WAVES][16 * WT_ROW];
-  __shared__ f32x4_t s_part[CO_PART_VECS];
+// LDS of one block, declared by the kernel and shared by both bodies.
+struct CoShared {
+  int* s_istart;
+  int* s_off;
+  int* s_next;
+  int* s_maxm;
+  int* s_done;
+  int* s_fin;
+  CoItem* s_info;
+  int (*s_tok)[16 * CO_NT];
+  char (*s_wt)[16 * WT_ROW];
+  f32x4_t* s_part;
+};
 
+// KEEP: items whose tile has later passes read their weights with the
+// ordinary (temporal) policy so that those passes, adjacent items on the same
+// XCD, find them in L2; everything else streams them non-temporally.  A
+// launch with no group above 16 rows has one pass per tile and runs the body
+// without that choice.
+template <typename T, int MODE, bool FULLK, bool KEEP>
+__device__ __forceinline__ void coop_body(const XArgs& a, const CoShared& sh) {
+  int* s_istart = sh.s_istart;
+  int* s_off = sh.s_off;
+  int& s_next = *sh.s_next;
+  int* s_done = sh.s_done;
+  int* s_fin = sh.s_fin;
+  CoItem* s_info = sh.s_info;
+  int (*s_tok)[16 * CO_NT] = sh.s_tok;
+  char (*s_wt)[16 * WT_ROW] = sh.s_wt;
+  f32x4_t* s_part = sh.s_part;
   const int wv = uni(threadIdx.x / WAVE);
   const int l = lane_id();
   const int lrow = l & 15;
@@ -175,29 +194,12 @@ __global__ __launch_bounds__(CO_THREADS) void expert_coop_kernel(XArgs a) {
   const int nb = gridDim.x / CO_XCD;    // blocks per XCD (the grid is a multiple of 8)
   const int xcd = blockIdx.x % CO_XCD;
   const int jb = blockIdx.x / CO_XCD;
-
-  item_prefix<CO_NT>(a.offsets, a.n_groups, a.n_quads, a.tile_nt, a.tile_min, a.tile_m_min, s_istart, s_off,
-                     &s_ntx);
-  if (wv == 0) {
-    // largest group held here, for the token tiles the partial slots need
-    int m = 0;
-    for (int g = l; g < a.n_groups; g += WAVE) m = max(m, a.offsets[g + 1] - a.offsets[g]);
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) m = max(m, __shfl_xor(m, d, WAVE));
-    if (l == 0) s_maxm = m;
-  }
-  if (threadIdx.x == 0) {
-    s_next = 0;
-    for (int r = 0; r < CO_RING_MAX; ++r) s_done[r] = 0;
-  }
-  if (threadIdx.x < CO_INFO) s_info[threadIdx.x].tag = -1;
-  __syncthreads();
   const int n_items = s_istart[a.n_groups];
   const uint32_t row_bytes = static_cast<uint32_t>(a.K) * sizeof(T);
   const char* act = reinterpret_cast<const char*>(a.act);
   const int kbytes = a.kfrag_total * FRAG_BYTES;
   char* tile = s_wt[wv];
-  const int ntx = uni(s_maxm) > 16 ? 2 : 1;  // token tiles a partial slot holds
+  const int ntx = CO_NT;                      // token tiles a partial slot holds
   const int U = a.nck * a.sub;                // units per item
   const int slot_vecs = U * ntx * WAVE;
   const int R = max(1, min(CO_RING_MAX, CO_PART_VECS / slot_vecs));
@@ -248,6 +250,7 @@ __global__ __launch_bounds__(CO_THREADS) void expert_coop_kernel(XArgs a) {
     it.n0 = uni(d.n0);
     it.n_sub = uni(d.n_sub);
     it.sub_bytes = sub_bytes;
+    it.keep = uni(d.pad);
     it.wbase = reinterpret_cast<const char*>(a.w) + static_cast<size_t>(uni(d.first_row)) * row_bytes;
 #pragma unroll
     for (int j = 0; j < 4; ++j) it.woff[j] = woff[j];
@@ -284,7 +287,8 @@ __global__ __launch_bounds__(CO_THREADS) void expert_coop_kernel(XArgs a) {
   if (item != ITEM_END) {
     load_item(k, item, cur);
     const int s = u / a.nck, c = u - (u / a.nck) * a.nck;
-    if constexpr (FULLK) wload_full(tile_chunk(cur, s, c), cur.woff, w0);
+    if constexpr (FULLK && KEEP) wload_full_keep(tile_chunk(cur, s, c), cur.woff, w0, cur.keep);
+    else if constexpr (FULLK) wload_full(tile_chunk(cur, s, c), cur.woff, w0);
     else wload(tile_chunk(cur, s, c), cur.woff, kbytes - c * CHUNK_BYTES, lrow, w0);
     if constexpr (FULLK)
       xload_full<CO_NT>(act + c * CHUNK_BYTES, cur.xoff, cur.m_end - cur.t0, x);
@@ -312,7 +316,9 @@ __global__ __launch_bounds__(CO_THREADS) void expert_coop_kernel(XArgs a) {
       else nxt = cur;                                                                           \
       const int s2 = u2 / a.nck;                                                                \
       const int c2 = u2 - s2 * a.nck;                                                           \
-      if constexpr (FULLK)                                                                      \
+      if constexpr (FULLK && KEEP)                                                              \
+        wload_full_keep(tile_chunk(nxt, s2, c2), nxt.woff, WN, nxt.keep);                       \
+      else if constexpr (FULLK)                                                                 \
         wload_full(tile_chunk(nxt, s2, c2), nxt.woff, WN);                                      \
       else                                                                                      \
         wload(tile_chunk(nxt, s2, c2), nxt.woff, kbytes - c2 * CHUNK_BYTES, lrow, WN);          \
@@ -385,7 +391,42 @@ __global__ __launch_bounds__(CO_THREADS) void expert_coop_kernel(XArgs a) {
     }
   }
 #undef CO_STEP
+}
 
+template <typename T, int MODE, bool FULLK>
+__global__ __launch_bounds__(CO_THREADS) void expert_coop_kernel(XArgs a) {
+  __shared__ int s_istart[MAX_GROUPS + 1];
+  __shared__ int s_off[MAX_GROUPS + 1];
+  __shared__ int s_ntx;
+  __shared__ int s_next, s_maxm;
+  __shared__ int s_done[CO_RING_MAX], s_fin[CO_RING_MAX];
+  __shared__ __attribute__((aligned(16))) CoItem s_info[CO_INFO];
+  __shared__ int s_tok[CO_INFO][16 * CO_NT];
+  __shared__ __attribute__((aligned(16))) char s_wt[CO_WAVES][16 * WT_ROW];
+  __shared__ f32x4_t s_part[CO_PART_VECS];
+  const int l = lane_id();
+
+  item_prefix<CO_NT>(a.offsets, a.n_groups, a.n_quads, a.tile_nt, a.tile_min, a.tile_m_min, s_istart, s_off,
+                     &s_ntx);
+  if (threadIdx.x < WAVE) {
+    // largest group held here: more than 16 rows means tiles with later passes
+    int m = 0;
+    for (int g = l; g < a.n_groups; g += WAVE) m = max(m, a.offsets[g + 1] - a.offsets[g]);
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) m = max(m, __shfl_xor(m, d, WAVE));
+    if (l == 0) s_maxm = m;
+  }
+  if (threadIdx.x == 0) {
+    s_next = 0;
+    for (int r = 0; r < CO_RING_MAX; ++r) s_done[r] = 0;
+  }
+  if (threadIdx.x < CO_INFO) s_info[threadIdx.x].tag = -1;
+  __syncthreads();
+  const CoShared sh{s_istart, s_off, &s_next, &s_maxm, s_done, s_fin, s_info, s_tok, s_wt, s_part};
+  if (uni(s_maxm) > 16)
+    coop_body<T, MODE, FULLK, true>(a, sh);
+  else
+    coop_body<T, MODE, FULLK, false>(a, sh);
 }
 
 // ---------------------------------------------------------------- host side

@@ -126,6 +126,7 @@ struct WItem {
   int n_sub;               // tiles of the item inside the matrix (1..SUB)
   const char* wbase;       // the item's first weight row (wave-uniform)
   uint32_t sub_bytes;      // byte distance between consecutive tiles of the item
+  int keep;                // block-cooperative kernel: weights read with the temporal policy
   uint32_t woff[4];        // lane: row 4j + lq of a tile, + 16*lrow, relative to the tile's base
   uint32_t xoff[NT];       // lane: its token's activation row, + 16*lq, relative to the activations
 };
@@ -230,6 +231,18 @@ __device__ __forceinline__ void wload_part(const char* cbase, const uint32_t (&w
   for (int i = 0; i < CHUNK_FRAGS; ++i) {
     const int col = 256 * (i / 4) + 16 * lrow;
     w[i] = ldg_nt(cbase, woff[i % 4] + (col < valid ? 256 * (i / 4) : -16 * lrow));
+  }
+}
+// The same loads with the ordinary (temporal) policy when `keep`: the lines
+// stay in L2 for later passes over the same tile.
+__device__ __forceinline__ void wload_full_keep(const char* cbase, const uint32_t (&woff)[4], uint4 (&w)[CHUNK_FRAGS],
+                                                bool keep) {
+  if (keep) {
+#pragma unroll
+    for (int i = 0; i < CHUNK_FRAGS; ++i) w[i] = ldg(cbase + 256 * (i / 4), woff[i % 4]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < CHUNK_FRAGS; ++i) w[i] = ldg_nt(cbase + 256 * (i / 4), woff[i % 4]);
   }
 }
 __device__ __forceinline__ void wload_full(const char* cbase, const uint32_t (&woff)[4], uint4 (&w)[CHUNK_FRAGS]) {
