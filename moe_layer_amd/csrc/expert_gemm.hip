@@ -205,7 +205,12 @@ __device__ __forceinline__ void split_reduce(const XArgs& a, const WItem<NT>& it
 }
 
 // The streaming part of the kernel, after the item table is built.
-template <typename T, int MODE, int NT, int SUB, bool FULLK>
+// KEEP: items whose tiles have later passes read their weights with the
+// ordinary (temporal) policy, so the passes that follow (adjacent items,
+// running at the same time on the same XCD) find them in L2; all other weights
+// stream non-temporally.  Launches where every group fits one pass run the
+// body without that choice.
+template <typename T, int MODE, int NT, int SUB, bool FULLK, bool KEEP>
 __device__ __forceinline__ void stream_body(const XArgs& a, const int* s_istart, const int* s_off, char* tile,
                                             int wv, int l, int lrow, int lq) {
   const long long Q = static_cast<long long>(uni(s_istart[a.n_groups])) * a.nck;
@@ -256,7 +261,9 @@ __device__ __forceinline__ void stream_body(const XArgs& a, const int* s_istart,
     witem_token_ids<T, MODE, NT>(a, lrow, nxt, raw_n);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (FULLK)
+  if constexpr (FULLK && KEEP)
+    wload_full_keep(tile_chunk(cur, 0, c), cur.woff, w0, cur.keep);
+  else if constexpr (FULLK)
     wload_full(tile_chunk(cur, 0, c), cur.woff, w0);
   else
     wload(tile_chunk(cur, 0, c), cur.woff, kbytes - c * CHUNK_BYTES, lrow, w0);
@@ -282,17 +289,22 @@ __device__ __forceinline__ void stream_body(const XArgs& a, const int* s_istart,
     {                                                                                     \
       const char* nb;                                                                     \
       int nv;                                                                             \
+      bool nk;                                                                            \
       if (S + 1 < SUB) {                                                                  \
         nb = tile_chunk(cur, S + 1, c);                                                   \
         nv = cvalid;                                                                      \
+        nk = cur.keep;                                                                    \
       } else {                                                                            \
         const char* b_next = tile_chunk(cur, 0, c + 1);                                   \
         const char* b_item = tile_chunk(nxt, 0, 0);                                       \
         const char* b_same = tile_chunk(cur, 0, c);                                       \
         nb = !last ? b_next : (have_nxt ? b_item : b_same);                               \
         nv = !last ? cvalid - CHUNK_BYTES : (have_nxt ? kbytes : cvalid);                 \
+        nk = (last && have_nxt) ? nxt.keep : cur.keep;                                    \
       }                                                                                   \
-      if constexpr (FULLK)                                                                \
+      if constexpr (FULLK && KEEP)                                                        \
+        wload_full_keep(nb, cur.woff, WN, nk);                                            \
+      else if constexpr (FULLK)                                                           \
         wload_full(nb, cur.woff, WN);                                                     \
       else                                                                                \
         wload(nb, cur.woff, nv, lrow, WN);                                                \
@@ -393,7 +405,7 @@ template <typename T, int MODE, int NT, int SUB, bool FULLK>
 __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   __shared__ int s_istart[MAX_GROUPS + 1];
   __shared__ int s_off[MAX_GROUPS + 1];
-  __shared__ int s_ntx;
+  __shared__ int s_ntx, s_maxm;
   __shared__ __attribute__((aligned(16))) char s_wt[XW_WAVES][16 * WT_ROW];
 
   const int wv = uni(threadIdx.x / WAVE);
@@ -402,14 +414,27 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
   const int lq = l >> 4;
 
   item_prefix<NT>(a.offsets, a.n_groups, a.n_quads, a.tile_nt, a.tile_min, a.tile_m_min, s_istart, s_off, &s_ntx);
+  if constexpr (NT <= 2) {
+    if (threadIdx.x < WAVE) {
+      // largest group: more than one pass of 16 * NT rows means tiles with later passes
+      int m = 0;
+      for (int g = l; g < a.n_groups; g += WAVE) m = max(m, a.offsets[g + 1] - a.offsets[g]);
+#pragma unroll
+      for (int d = 1; d < WAVE; d <<= 1) m = max(m, __shfl_xor(m, d, WAVE));
+      if (l == 0) s_maxm = m;
+    }
+  }
   __syncthreads();  // the only barrier; waves are independent from here on
   if constexpr (NT == 4) {
     if (uni(s_ntx) == 4)
-      stream_body<T, MODE, 4, SUB, FULLK>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
+      stream_body<T, MODE, 4, SUB, FULLK, false>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
     else
-      stream_body<T, MODE, 2, SUB, FULLK>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
+      stream_body<T, MODE, 2, SUB, FULLK, false>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
   } else {
-    stream_body<T, MODE, NT, SUB, FULLK>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
+    if (FULLK && uni(s_maxm) > 16 * NT)
+      stream_body<T, MODE, NT, SUB, FULLK, FULLK>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
+    else
+      stream_body<T, MODE, NT, SUB, FULLK, false>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
   }
 }
 

@@ -126,7 +126,7 @@ struct WItem {
   int n_sub;               // tiles of the item inside the matrix (1..SUB)
   const char* wbase;       // the item's first weight row (wave-uniform)
   uint32_t sub_bytes;      // byte distance between consecutive tiles of the item
-  int keep;                // block-cooperative kernel: weights read with the temporal policy
+  int keep;                // the tile has later passes: weights read with the temporal policy
   uint32_t woff[4];        // lane: row 4j + lq of a tile, + 16*lrow, relative to the tile's base
   uint32_t xoff[NT];       // lane: its token's activation row, + 16*lq, relative to the activations
 };
@@ -148,6 +148,7 @@ __device__ __forceinline__ void witem_weights(const XArgs& a, const int* s_istar
   const int m = uni(s_off[lo + 1]) - it.row0;
   const int ps = pass_rows<NT>(m);
   const int np = (m + ps - 1) / ps;
+  it.keep = np > 1;   // later passes over the same tiles follow
   const int local = item - uni(s_istart[lo]);
   const int nq = local / np;
   it.t0 = (local - nq * np) * ps;
