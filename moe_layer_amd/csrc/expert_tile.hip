@@ -264,12 +264,22 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
     // ---- K loop: stage s is fetched two stages ahead into registers
     // (a chunk past the end of K re-reads the row's last valid 64 bytes;
     // lstore zeroes it)
+    // A group with more than one token tile reads each weight tile once per
+    // token tile; those tiles run side by side on one XCD, so their weights
+    // are read with the ordinary policy and the later reads find them in L2.
+    // Every other weight tile is streamed once, non-temporally.
+    const bool keep = n_mt > 1;
     auto gload = [&](int s, uint4 (&R)[2 * TL_LD]) {
       const int delta = min(0, kbytes - 16 - s * TL_KB - 16 * lc) & ~63;
       const char* wb = wbase + s * TL_KB;
       const char* xb = act + s * TL_KB;
+      if (keep) {
 #pragma unroll
-      for (int i = 0; i < TL_LD; ++i) R[i] = tl_ldg_nt(wb, woff[i] + delta);
+        for (int i = 0; i < TL_LD; ++i) R[i] = tl_ldg(wb, woff[i] + delta);
+      } else {
+#pragma unroll
+        for (int i = 0; i < TL_LD; ++i) R[i] = tl_ldg_nt(wb, woff[i] + delta);
+      }
 #pragma unroll
       for (int i = 0; i < TL_LD; ++i) R[TL_LD + i] = tl_ldg(xb, xoff[i] + delta);
     };
