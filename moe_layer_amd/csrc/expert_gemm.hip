@@ -265,6 +265,8 @@ __device__ __forceinline__ void stream_body(const XArgs& a, const int* s_istart,
     wload_full_keep(tile_chunk(cur, 0, c), cur.woff, w0, cur.keep);
   else if constexpr (FULLK)
     wload_full(tile_chunk(cur, 0, c), cur.woff, w0);
+  else if constexpr (KEEP)
+    wload_part_keep(tile_chunk(cur, 0, c), cur.woff, kbytes - c * CHUNK_BYTES, lrow, w0, cur.keep);
   else
     wload(tile_chunk(cur, 0, c), cur.woff, kbytes - c * CHUNK_BYTES, lrow, w0);
   __builtin_amdgcn_sched_barrier(0);
@@ -306,6 +308,8 @@ __device__ __forceinline__ void stream_body(const XArgs& a, const int* s_istart,
         wload_full_keep(nb, cur.woff, WN, nk);                                            \
       else if constexpr (FULLK)                                                           \
         wload_full(nb, cur.woff, WN);                                                     \
+      else if constexpr (KEEP)                                                            \
+        wload_part_keep(nb, cur.woff, nv, lrow, WN, nk);                                  \
       else                                                                                \
         wload(nb, cur.woff, nv, lrow, WN);                                                \
     }                                                                                     \
@@ -431,8 +435,8 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
     else
       stream_body<T, MODE, 2, SUB, FULLK, false>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
   } else {
-    if (FULLK && uni(s_maxm) > 16 * NT)
-      stream_body<T, MODE, NT, SUB, FULLK, FULLK>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
+    if (uni(s_maxm) > 16 * NT)
+      stream_body<T, MODE, NT, SUB, FULLK, true>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
     else
       stream_body<T, MODE, NT, SUB, FULLK, false>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
   }

@@ -250,6 +250,19 @@ __device__ __forceinline__ void wload_full(const char* cbase, const uint32_t (&w
 #pragma unroll
   for (int i = 0; i < CHUNK_FRAGS; ++i) w[i] = ldg_nt(cbase + 256 * (i / 4), woff[i % 4]);
 }
+// The partial-chunk loads with the ordinary (temporal) policy when `keep`.
+__device__ __forceinline__ void wload_part_keep(const char* cbase, const uint32_t (&woff)[4], int valid,
+                                                int lrow, uint4 (&w)[CHUNK_FRAGS], bool keep) {
+  if (keep) {
+#pragma unroll
+    for (int i = 0; i < CHUNK_FRAGS; ++i) {
+      const int col = 256 * (i / 4) + 16 * lrow;
+      w[i] = ldg(cbase, woff[i % 4] + (col < valid ? 256 * (i / 4) : -16 * lrow));
+    }
+  } else {
+    wload_part(cbase, woff, valid, lrow, w);
+  }
+}
 // One load sequence for full and partial chunks (the partial form gives the
 // full form's addresses when valid >= 512).  Loads behind a branch land in
 // different registers on the two paths; the join then copies registers and
