@@ -582,8 +582,8 @@ static void launch_tm(XArgs a, int nt, int sub, hipStream_t s) {
 template <int MODE>
 static void launch_mode(int dtype, XArgs a, int T, int kk, void* ws, hipStream_t s) {
   a.tile_nt = expert_tile_used(T, dtype) ? expert_tile_nt(MODE == XMODE_UP, a.H, a.I_loc) : 0;
-  a.tile_min = expert_tile_min_tiles();
   a.tile_m_min = expert_tile_m_min(T, kk, a.n_groups);
+  a.tile_min = expert_tile_min_tiles(a.tile_m_min);
   const XShape sh = x_shape(MODE, a.H, a.I_loc, dtype);
   a.n_tiles = sh.n_tiles;
   a.kfrag_total = sh.kfrag_total;

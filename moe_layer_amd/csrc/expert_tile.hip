@@ -476,7 +476,12 @@ static size_t tl_ctr_bytes(int T, int kk, int n_groups, int H, int I) {
 // XCD count, at most TL_MAX_GRID); the tile path runs only when the groups
 // above m_min make at least a third of a tile per compute unit (fewer tiles
 // leave most of the chip idle, and the wave-streaming kernel does better).
-static int tile_min_tiles() { return (device_cu_count() + 2) / 3; }
+// When the wave-streaming kernel takes 64-row passes (m_min is
+// TILE_M_MIN_WIDE) it reads a hot group's weights few enough times, from L2,
+// that the tile path needs a tile per compute unit to be worth its launch.
+static int tile_min_tiles(int m_min) {
+  return m_min >= TILE_M_MIN_WIDE ? device_cu_count() : (device_cu_count() + 2) / 3;
+}
 
 template <int MODE>
 static void tile_launch(TArgs a, int T, void* ws, hipStream_t s) {
@@ -484,7 +489,7 @@ static void tile_launch(TArgs a, int T, void* ws, hipStream_t s) {
   if (grid > TL_MAX_GRID) grid = TL_MAX_GRID;
   grid = grid / TL_XCD * TL_XCD;
   if (grid < TL_XCD) grid = TL_XCD;
-  a.min_tiles = tile_min_tiles();
+  a.min_tiles = tile_min_tiles(a.m_min);
   a.ctr = static_cast<int*>(ws);
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + tl_ctr_bytes(T, a.kk, a.n_groups, a.H, a.I_loc));
   hipLaunchKernelGGL(expert_tile_kernel<MODE>, dim3(static_cast<unsigned>(grid)), dim3(TL_THREADS), 0, s, a);
@@ -492,7 +497,7 @@ static void tile_launch(TArgs a, int T, void* ws, hipStream_t s) {
 
 bool expert_tile_used(int T, int dtype) { return dtype == 1 && T > TILE_T_MIN; }
 
-int expert_tile_min_tiles() { return tile_min_tiles(); }
+int expert_tile_min_tiles(int m_min) { return tile_min_tiles(m_min < TILE_M_MIN ? TILE_M_MIN : m_min); }
 
 size_t expert_tile_workspace_bytes(int T, int kk, int n_groups, int H, int I, int dtype) {
   if (!expert_tile_used(T, dtype)) return 0;

@@ -73,7 +73,7 @@ void launch_expert_down(int dtype, const void* a, const int32_t* offsets, int n_
 // every group with more than m_min sorted rows (TILE_M_MIN, or
 // TILE_M_MIN_WIDE when the wave-streaming kernel holds four token tiles and
 // takes up to 64 rows in one pass), provided those groups
-// make at least expert_tile_min_tiles() tiles of TILE_ROWS token rows x
+// make at least expert_tile_min_tiles(m_min) tiles of TILE_ROWS token rows x
 // (up: 64 intermediate columns; down: 128 output features); the
 // wave-streaming kernel then skips exactly those groups.  Both kernels take
 // this decision on the device, from the same counts and the same formula.
@@ -82,7 +82,7 @@ constexpr int TILE_M_MIN_WIDE = 64;
 constexpr int TILE_T_MIN = 256;
 constexpr int TILE_ROWS = 128;
 inline int expert_tile_nt(bool up, int H, int I) { return up ? (I + 63) / 64 : (H + 127) / 128; }
-int expert_tile_min_tiles();
+int expert_tile_min_tiles(int m_min);
 // The row threshold of the LDS-tiled kernels for this launch (both kernels use it).
 int expert_tile_m_min(int T, int kk, int n_groups);
 bool expert_tile_used(int T, int dtype);

@@ -91,6 +91,23 @@ def test_four_token_tiles(T, E, k, hot, dtype):
     gh.check_layer(d, cfg, g)
 
 
+# A launch whose wave-streaming kernel holds four token tiles runs the
+# LDS-tiled kernels only with a tile per compute unit: 600 tokens over 8
+# experts (137-166 rows each, two token tiles) with I = 1024 and H = 2048
+# make 256 up and 256 down tiles (one per MI355X compute unit), so the tiled
+# kernels run and take every group, and the wave-streaming launch, deciding
+# by the same device-side rule, finds nothing left.
+def test_four_token_tiles_with_tiled_groups():
+    import gpu_helpers as gh
+    cfg = small(H=2048, E=8, k=2, I=1024, T=600)
+    d = make_layer_inputs(cfg, 600, routing="uniform", seed=77)
+    print("[case] four token tiles with tiled groups T=600 E=8 k=2 H=2048 I=1024", flush=True)
+    g = gh.gpu_layer(d, cfg)
+    counts = g["counts"]
+    assert (counts > 128).sum() >= 4, counts   # several groups past one 128-row tile
+    gh.check_layer(d, cfg, g)
+
+
 @pytest.mark.parametrize("n_shared,renorm", [(2, False), (1, True)])
 def test_shared_experts(n_shared, renorm):
     import gpu_helpers as gh
