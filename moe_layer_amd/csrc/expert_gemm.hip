@@ -210,11 +210,12 @@ __device__ __forceinline__ void split_reduce(const XArgs& a, const WItem<NT>& it
 // running at the same time on the same XCD) find them in L2; all other weights
 // stream non-temporally.  Launches where every group fits one pass run the
 // body without that choice.
+// Blocks 0 .. nblk-1 of the grid take part.
 template <typename T, int MODE, int NT, int SUB, bool FULLK, bool KEEP>
 __device__ __forceinline__ void stream_body(const XArgs& a, const int* s_istart, const int* s_off, char* tile,
-                                            int wv, int l, int lrow, int lq) {
+                                            int wv, int l, int lrow, int lq, int nblk) {
   const long long Q = static_cast<long long>(uni(s_istart[a.n_groups])) * a.nck;
-  const int W = static_cast<int>(min(static_cast<long long>(a.waves), (Q + MIN_CPW - 1) / MIN_CPW));
+  const int W = static_cast<int>(min(static_cast<long long>(nblk) * XW_WAVES, (Q + MIN_CPW - 1) / MIN_CPW));
   // Range index.  Blocks are dealt to the 8 XCDs in turn, so XCD x holds the
   // blocks b with b % 8 == x; it takes the contiguous ranges [x*W/8,
   // (x+1)*W/8), first one wave of each of its blocks, then the next.  Its
@@ -223,14 +224,14 @@ __device__ __forceinline__ void stream_body(const XArgs& a, const int* s_istart,
   // XCD's L2.  The assignment covers every range whenever the grid is a
   // multiple of 8 (always here; otherwise wave w takes range w).
   int w;
-  if (gridDim.x % 8 == 0) {
+  if (nblk % 8 == 0) {
     const int xcd = blockIdx.x % 8;
-    const int kx = wv * (gridDim.x / 8) + blockIdx.x / 8;
+    const int kx = wv * (nblk / 8) + blockIdx.x / 8;
     const int xlo = static_cast<int>(static_cast<long long>(W) * xcd / 8);
     if (kx >= static_cast<int>(static_cast<long long>(W) * (xcd + 1) / 8) - xlo) return;  // wave-uniform
     w = xlo + kx;
   } else {
-    w = wv * gridDim.x + blockIdx.x;
+    w = wv * nblk + blockIdx.x;
     if (w >= W) return;  // wave-uniform
   }
   const long long q0 = Q * w / W;
@@ -429,16 +430,29 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
     }
   }
   __syncthreads();  // the only barrier; waves are independent from here on
+  const int nblk = static_cast<int>(gridDim.x);
   if constexpr (NT == 4) {
     if (uni(s_ntx) == 4)
-      stream_body<T, MODE, 4, SUB, FULLK, false>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
+      stream_body<T, MODE, 4, SUB, FULLK, false>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq, nblk);
     else
-      stream_body<T, MODE, 2, SUB, FULLK, false>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
+      stream_body<T, MODE, 2, SUB, FULLK, false>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq, nblk);
   } else {
-    if (uni(s_maxm) > 16 * NT)
-      stream_body<T, MODE, NT, SUB, FULLK, true>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
-    else
-      stream_body<T, MODE, NT, SUB, FULLK, false>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq);
+    if (uni(s_maxm) > 16 * NT) {
+      stream_body<T, MODE, NT, SUB, FULLK, true>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq, nblk);
+    } else {
+      // Every group in one pass and a grid of two blocks per CU: only the
+      // first half of the grid (the blocks dispatched first, one per CU)
+      // streams, provided each of its waves still gets three chunk steps.
+      // With both, the waves of the block dispatched second ended 7 us after
+      // those of the first (TP share, B = 64: medians 35.9 and 29.1 us), and
+      // one block per CU gave the shorter launch.  Launches with later
+      // passes, or with fewer steps, keep both: there, one block per CU was
+      // slower.
+      const long long q = static_cast<long long>(uni(s_istart[a.n_groups])) * a.nck;
+      const int half = (a.halve && q >= 3LL * (nblk / 2) * XW_WAVES) ? nblk / 2 : nblk;
+      if (static_cast<int>(blockIdx.x) < half)
+        stream_body<T, MODE, NT, SUB, FULLK, false>(a, s_istart, s_off, s_wt[wv], wv, l, lrow, lq, half);
+    }
   }
 }
 
@@ -558,6 +572,7 @@ template <typename T, int MODE, int NT, int SUB, bool FULLK>
 static void launch_k(XArgs a, hipStream_t s) {
   const int grid = resident_blocks<T, MODE, NT, SUB, FULLK>();
   a.waves = grid * XW_WAVES;
+  a.halve = (grid == 2 * device_cu_count() && grid % 16 == 0) ? 1 : 0;
   a.n_quads = (a.n_tiles + SUB - 1) / SUB;
   hipLaunchKernelGGL((expert_wave_kernel<T, MODE, NT, SUB, FULLK>), dim3(grid), dim3(XW_WAVES * WAVE), 0, s, a);
 }

@@ -38,6 +38,7 @@ struct XArgs {
   int* ctr;                // per-item arrival counters (zero between calls)
   float* part;             // per-wave partial tiles: [wave][2][SUB][NT][64 lanes][4]
   int sub;                 // block-cooperative kernel: weight tiles per item (runtime)
+  int halve;               // wave-streaming kernel: the grid holds two blocks per CU (a multiple of 16 blocks)
 };
 
 // Token rows per pass of a group with m rows: 16, or 16*NT when the kernel
