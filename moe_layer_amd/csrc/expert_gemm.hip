@@ -617,6 +617,13 @@ static void launch_mode(int dtype, XArgs a, int T, int kk, void* ws, hipStream_t
     }
   }
   const int nt = pick_nt(T, kk, a.n_groups);
+  // Short W2 rows (the TP view's I / P slices): whole tiles per step, in
+  // passes of 16 or 32 rows (where this kernel would take 64-row passes,
+  // 384 <= T < 768, the short-row kernel's 32-row passes were slower).
+  if (MODE == XMODE_DOWN && nt <= 2 && expert_short_down_ok(dtype, a.H, a.I_loc)) {
+    launch_expert_down_short(a, nt, s);
+    return;
+  }
   const int sub = pick_sub(nt, sh.kfrag_total);
   if (dtype == 1)
     launch_tm<uint16_t, MODE>(a, nt, sub, s);

@@ -345,5 +345,11 @@ __device__ __forceinline__ void wmma_part(const uint4 (&w)[CHUNK_FRAGS], const u
 // needs no workspace.
 int expert_coop_sub(int nck);
 void launch_expert_coop_up(XArgs a, hipStream_t s);
+// Down-projection for W2 rows of at most 512 bytes (expert_short.hip):
+// whether it takes these shapes, and the launch (a's shape and tile-rule
+// fields set as for the wave-streaming kernel; NT = 1 or 2 token tiles per
+// pass).  It needs no workspace.
+bool expert_short_down_ok(int dtype, int H, int I);
+void launch_expert_down_short(const XArgs& a, int nt, hipStream_t s);
 
 }  // namespace moe

@@ -108,6 +108,32 @@ def test_four_token_tiles_with_tiled_groups():
     gh.check_layer(d, cfg, g)
 
 
+# Down-projections whose W2 rows are at most 512 bytes (bf16, I' <= 256) take
+# whole 16-row tiles per step with the pass's token fragments held in
+# registers: every row length (1..8 fragments of 64 bytes), passes of 16 and
+# 32 rows, a hot expert with several passes, empty experts, and ranges of
+# steps that cross from one pass or group to the next (H = 4096: 256 tiles per
+# pass, a few thousand steps over the chip's waves).
+@pytest.mark.parametrize("T,E,k,H,I,hot", [
+    (64, 16, 8, 4096, 192, False),    # the TP share's row length; ~32 rows per expert, one or two passes
+    (40, 16, 4, 1024, 32, True),      # one fragment per row; a hot expert of 40 rows (passes of 32)
+    (12, 32, 2, 2048, 96, False),     # three fragments; passes of 16 rows, empty experts
+    (200, 8, 3, 512, 256, True),      # eight fragments, 32 tiles per pass; a 200-row expert
+    (300, 8, 2, 1024, 160, False),    # five fragments; T above 256 (the tiled kernels' rule is evaluated)
+])
+def test_short_row_down(T, E, k, H, I, hot):
+    import gpu_helpers as gh
+    cfg = small(H=H, E=E, k=k, I=I, T=T)
+    d = make_layer_inputs(cfg, T, routing="uniform", seed=T + I)
+    if hot:
+        b = np.zeros(E, dtype=np.float32)
+        b[1] = 40.0        # every token picks expert 1 first
+        d["gate_bias"] = b
+    print(f"[case] short-row down T={T} E={E} k={k} H={H} I={I} hot={hot}", flush=True)
+    g = gh.gpu_layer(d, cfg)
+    gh.check_layer(d, cfg, g)
+
+
 @pytest.mark.parametrize("n_shared,renorm", [(2, False), (1, True)])
 def test_shared_experts(n_shared, renorm):
     import gpu_helpers as gh
