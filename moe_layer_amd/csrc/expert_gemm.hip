@@ -594,9 +594,23 @@ static void launch_tm(XArgs a, int nt, int sub, hipStream_t s) {
   else launch_t<T, MODE, 1, 1>(a, s);
 }
 
+// Token tiles per pass of the short-row down kernel, from the mean rows per
+// group: it holds a pass's token fragments in registers and takes every
+// group, so passes of 64 rows serve the larger batches.
+static int short_nt(int T, int kk, int n_groups) {
+  const double mean = static_cast<double>(T) * kk / n_groups;
+  if (T <= 16 || mean <= 12.0) return 1;
+  return mean <= 24.0 ? 2 : 4;
+}
+
+// Whether the down-projection of these shapes runs entirely in the short-row
+// kernel (then no LDS-tiled launch precedes it).
+static bool down_short(int dtype, int H, int I) { return expert_short_down_ok(dtype, H, I); }
+
 template <int MODE>
 static void launch_mode(int dtype, XArgs a, int T, int kk, void* ws, hipStream_t s) {
-  a.tile_nt = expert_tile_used(T, dtype) ? expert_tile_nt(MODE == XMODE_UP, a.H, a.I_loc) : 0;
+  const bool short_rows = MODE == XMODE_DOWN && down_short(dtype, a.H, a.I_loc);
+  a.tile_nt = (expert_tile_used(T, dtype) && !short_rows) ? expert_tile_nt(MODE == XMODE_UP, a.H, a.I_loc) : 0;
   a.tile_m_min = expert_tile_m_min(T, kk, a.n_groups);
   a.tile_min = expert_tile_min_tiles(a.tile_m_min);
   const XShape sh = x_shape(MODE, a.H, a.I_loc, dtype);
@@ -616,14 +630,12 @@ static void launch_mode(int dtype, XArgs a, int T, int kk, void* ws, hipStream_t
       return;
     }
   }
-  const int nt = pick_nt(T, kk, a.n_groups);
-  // Short W2 rows (the TP view's I / P slices): whole tiles per step, in
-  // passes of 16 or 32 rows (where this kernel would take 64-row passes,
-  // 384 <= T < 768, the short-row kernel's 32-row passes were slower).
-  if (MODE == XMODE_DOWN && nt <= 2 && expert_short_down_ok(dtype, a.H, a.I_loc)) {
-    launch_expert_down_short(a, nt, s);
+  // Short W2 rows (the TP view's I / P slices): whole tiles per step.
+  if (short_rows) {
+    launch_expert_down_short(a, short_nt(T, kk, a.n_groups), s);
     return;
   }
+  const int nt = pick_nt(T, kk, a.n_groups);
   const int sub = pick_sub(nt, sh.kfrag_total);
   if (dtype == 1)
     launch_tm<uint16_t, MODE>(a, nt, sub, s);
@@ -663,7 +675,7 @@ void launch_expert_down(int dtype, const void* A, const int32_t* offsets, int n_
   a.K = I;
   a.I_loc = I;
   a.H = H;
-  if (expert_tile_used(T, dtype))
+  if (expert_tile_used(T, dtype) && !down_short(dtype, H, I))
     launch_expert_down_tiles(A, offsets, n_groups, T, kk, w2, H, I, y_pair, expert_tile_m_min(T, kk, n_groups),
                              static_cast<char*>(ws) + stream_workspace_bytes(T, kk, n_groups, H, I, dtype), s);
   launch_mode<XMODE_DOWN>(dtype, a, T, kk, ws, s);

@@ -65,23 +65,17 @@ __device__ __forceinline__ SStep sh_decode(const XArgs& a, const int* s_istart, 
   return d;
 }
 
-template <int KF, int NT>
-__global__ __launch_bounds__(SH_WAVES * WAVE) void expert_short_kernel(XArgs a) {
-  constexpr int RB = KF * FRAG_BYTES;  // bytes of a weight row and of an activation row
-  constexpr int PITCH = RB + 16;       // LDS row pitch of the transpose tile
-  __shared__ int s_istart[MAX_GROUPS + 1];
-  __shared__ int s_off[MAX_GROUPS + 1];
-  __shared__ int s_ntx;
-  __shared__ __attribute__((aligned(16))) char s_wt[SH_WAVES][16 * PITCH];
+template <int KF>
+constexpr int sh_pitch() { return KF * FRAG_BYTES + 16; }  // LDS row pitch of the transpose tile
 
-  const int wv = uni(threadIdx.x / WAVE);
+// The stream of one wave, after the step table is built (NT token tiles per pass).
+template <int KF, int NT>
+__device__ __forceinline__ void short_body(const XArgs& a, const int* s_istart, const int* s_off, char* tile, int wv) {
+  constexpr int RB = KF * FRAG_BYTES;  // bytes of a weight row and of an activation row
+  constexpr int PITCH = sh_pitch<KF>();
   const int l = lane_id();
   const int lrow = l & 15;
   const int lq = l >> 4;
-
-  // steps per group: its passes x H / 16 tiles (none for groups the tile kernels take)
-  item_prefix<NT>(a.offsets, a.n_groups, a.n_tiles, a.tile_nt, a.tile_min, a.tile_m_min, s_istart, s_off, &s_ntx);
-  __syncthreads();  // the only barrier; waves are independent from here on
 
   const int Q = uni(s_istart[a.n_groups]);
   const int nblk = static_cast<int>(gridDim.x);
@@ -104,7 +98,6 @@ __global__ __launch_bounds__(SH_WAVES * WAVE) void expert_short_kernel(XArgs a) 
   const char* wgt = reinterpret_cast<const char*>(a.w);
   const char* act = reinterpret_cast<const char*>(a.act);
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-  char* tile = s_wt[wv];
 
   // LDS byte offset of the 16 bytes this lane fetches with load i of a tile
   // (tile byte 1024 * i + 16 * l: row / RB, column % RB)
@@ -200,10 +193,32 @@ __global__ __launch_bounds__(SH_WAVES * WAVE) void expert_short_kernel(XArgs a) 
 #undef SH_STEP
 }
 
+template <int KF, int NT>
+__global__ __launch_bounds__(SH_WAVES * WAVE) void expert_short_kernel(XArgs a) {
+  __shared__ int s_istart[MAX_GROUPS + 1];
+  __shared__ int s_off[MAX_GROUPS + 1];
+  __shared__ int s_ntx;
+  __shared__ __attribute__((aligned(16))) char s_wt[SH_WAVES][16 * sh_pitch<KF>()];
+
+  const int wv = uni(threadIdx.x / WAVE);
+  // steps per group: its passes x H / 16 tiles (none for groups the tile
+  // kernels take); a kernel built for four token tiles runs two when no
+  // group holds more than 32 rows
+  item_prefix<NT>(a.offsets, a.n_groups, a.n_tiles, a.tile_nt, a.tile_min, a.tile_m_min, s_istart, s_off, &s_ntx);
+  __syncthreads();  // the only barrier; waves are independent from here on
+  if constexpr (NT == 4) {
+    if (uni(s_ntx) == 4) short_body<KF, 4>(a, s_istart, s_off, s_wt[wv], wv);
+    else short_body<KF, 2>(a, s_istart, s_off, s_wt[wv], wv);
+  } else {
+    short_body<KF, NT>(a, s_istart, s_off, s_wt[wv], wv);
+  }
+}
+
 template <int KF>
 void launch_kf(const XArgs& a, int nt, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(device_cu_count())), block(SH_WAVES * WAVE);
-  if (nt >= 2) hipLaunchKernelGGL((expert_short_kernel<KF, 2>), grid, block, 0, s, a);
+  if (nt >= 4) hipLaunchKernelGGL((expert_short_kernel<KF, 4>), grid, block, 0, s, a);
+  else if (nt == 2) hipLaunchKernelGGL((expert_short_kernel<KF, 2>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((expert_short_kernel<KF, 1>), grid, block, 0, s, a);
 }
 

@@ -69,7 +69,9 @@ void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, cons
 void launch_expert_down(int dtype, const void* a, const int32_t* offsets, int n_groups, int T,
                         int kk, const void* w2, int H, int I, void* y_pair, void* ws, hipStream_t s);
 // LDS-tiled expert kernels (expert_tile.hip) for groups holding many rows:
-// for bf16 and T > TILE_T_MIN, launch_expert_up/down first launch them on
+// for bf16 and T > TILE_T_MIN, launch_expert_up/down first launch them (the
+// down-projection not for W2 rows of at most 512 bytes, which the short-row
+// kernel of expert_short.hip takes whole) on
 // every group with more than m_min sorted rows (TILE_M_MIN, or
 // TILE_M_MIN_WIDE when the wave-streaming kernel holds four token tiles and
 // takes up to 64 rows in one pass), provided those groups
