@@ -596,11 +596,12 @@ static void launch_tm(XArgs a, int nt, int sub, hipStream_t s) {
 
 // Token tiles per pass of the short-row down kernel, from the mean rows per
 // group: it holds a pass's token fragments in registers and takes every
-// group, so passes of 64 rows serve the larger batches.
+// group, so passes of 64 and 128 rows serve the larger batches.
 static int short_nt(int T, int kk, int n_groups) {
   const double mean = static_cast<double>(T) * kk / n_groups;
   if (T <= 16 || mean <= 12.0) return 1;
-  return mean <= 24.0 ? 2 : 4;
+  if (mean <= 24.0) return 2;
+  return mean <= 64.0 ? 4 : 8;
 }
 
 // Whether the down-projection of these shapes runs entirely in the short-row

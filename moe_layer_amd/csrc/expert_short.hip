@@ -125,13 +125,17 @@ __device__ __forceinline__ void short_body(const XArgs& a, const int* s_istart, 
     }
   };
 
+  // With up to four token tiles the next pass's fragments are loaded ahead
+  // into a second set (xn); eight tiles leave no room for it, and those passes
+  // load theirs in place when the pass starts (once every H / 16 steps).
+  constexpr bool XN = NT <= 4;
   SStep cur = sh_decode<NT>(a, s_istart, s_off, q0);  // the step being multiplied
   SStep ld = cur;                                     // the next step to load
   int lqs = q0;
-  uint4 xc[NT][KF], xn[NT][KF];
+  uint4 xc[NT][KF], xn[XN ? NT : 1][KF];
   load_x(cur, xc);
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt)
+  for (int tt = 0; tt < (XN ? NT : 1); ++tt)
 #pragma unroll
     for (int f = 0; f < KF; ++f) xn[tt][f] = make_uint4(0u, 0u, 0u, 0u);  // written before it is read
   // Move `ld` to the next step; past the range it stays on the last one.  On
@@ -142,7 +146,7 @@ __device__ __forceinline__ void short_body(const XArgs& a, const int* s_istart, 
       ++lqs;
       if (++ld.j == a.n_tiles) {
         ld = sh_decode<NT>(a, s_istart, s_off, lqs);
-        load_x(ld, xn);
+        if constexpr (XN) load_x(ld, xn);
       }
     }
   };
@@ -179,8 +183,12 @@ __device__ __forceinline__ void short_body(const XArgs& a, const int* s_istart, 
     if (++cq >= q1) break;                                                                      \
     if (++cur.j == a.n_tiles) {                                                                 \
       cur = sh_decode<NT>(a, s_istart, s_off, cq);                                              \
-      _Pragma("unroll") for (int tt = 0; tt < NT; ++tt)                                         \
-        _Pragma("unroll") for (int f = 0; f < KF; ++f) xc[tt][f] = xn[tt][f];                   \
+      if constexpr (XN) {                                                                       \
+        _Pragma("unroll") for (int tt = 0; tt < (XN ? NT : 1); ++tt)                            \
+          _Pragma("unroll") for (int f = 0; f < KF; ++f) xc[tt][f] = xn[tt][f];                 \
+      } else {                                                                                  \
+        load_x(cur, xc);                                                                        \
+      }                                                                                         \
     }                                                                                           \
   }
   static_assert(SH_RING == 4, "the trip below is unrolled for four slots");
@@ -217,7 +225,8 @@ __global__ __launch_bounds__(SH_WAVES * WAVE) void expert_short_kernel(XArgs a) 
 template <int KF>
 void launch_kf(const XArgs& a, int nt, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(device_cu_count())), block(SH_WAVES * WAVE);
-  if (nt >= 4) hipLaunchKernelGGL((expert_short_kernel<KF, 4>), grid, block, 0, s, a);
+  if (nt >= 8) hipLaunchKernelGGL((expert_short_kernel<KF, 8>), grid, block, 0, s, a);
+  else if (nt >= 4) hipLaunchKernelGGL((expert_short_kernel<KF, 4>), grid, block, 0, s, a);
   else if (nt == 2) hipLaunchKernelGGL((expert_short_kernel<KF, 2>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((expert_short_kernel<KF, 1>), grid, block, 0, s, a);
 }
