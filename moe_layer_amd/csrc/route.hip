@@ -6,9 +6,14 @@
 // Phase A -- gate GEMM.  logits[t, e] = sum_h x[t, h] W_g[e, h] + b[e] is cut
 //   into units of 16 experts x 16 tokens x one K-slice; each wave computes a
 //   unit with 16x16 MFMA tiles (lane l: expert/token row l%16, bytes
-//   16*(l/16) of each 64-byte K fragment).  K is split into KS slices (a
-//   power of two; trailing slices may be empty) so that small batches still
-//   spread the gate matrix over many CUs.  With KS >= 8 a block's eight
+//   16*(l/16) of each 64-byte K fragment).  Both operands reach that layout
+//   through the wave's own LDS tile: each load instruction takes 256
+//   contiguous bytes of each of 4 rows (whole cache lines), and the tile,
+//   XOR-swizzled by row, hands every lane its row's fragment without bank
+//   conflicts.  (Loading the MFMA layout straight from memory, 64 bytes of
+//   each of 16 rows per instruction, ran phase A two times slower.)  K is
+//   split into KS slices (a power of two; trailing slices may be empty) so
+//   that small batches still spread the gate matrix over many CUs.  With KS >= 8 a block's eight
 //   waves take eight consecutive slices of one tile and the block sums them
 //   in LDS (wave order), so only KS / 8 partial tiles go through memory;
 //   with fewer slices each wave writes its own.  All blocks of one 16-token
@@ -49,7 +54,8 @@ namespace moe {
 
 constexpr int RT_WAVES = 8;
 constexpr int RT_THREADS = RT_WAVES * WAVE;
-constexpr int RT_CHUNK = 8;                // K fragments per inner step
+constexpr int RT_CHUNK = 4;                // K fragments per inner step (256 bytes of each row)
+constexpr int RT_TILE = 16 * RT_CHUNK * FRAG_BYTES;  // one operand's 16 rows of a step in LDS (4 KB)
 constexpr int RT_MAX_KS = 16;              // K slices at most (a power of two)
 constexpr int RT_KEY_CAP = 16 * MAX_E * 2; // 16-bit sort keys that fit the logit tile's LDS
 constexpr int RT_UNROLL = 4;               // logits each thread reduces per pass of phase B
@@ -77,6 +83,31 @@ struct RouteArgs {
   int n_tt;                // 16-token tiles
   int bpt;                 // blocks per token tile
 };
+
+// Phase-A staging.  A step covers 4 fragments (256 bytes, 16 chunks of 16
+// bytes) of 16 rows.  Load instruction i, lane (lrow = l % 16, lq = l / 16):
+// row 4i + lq, chunk lrow ^ (8 if lq >= 2), so each instruction reads 256
+// contiguous bytes of 4 rows.  In LDS, chunk c of row r sits at slot
+// c ^ swz(r) of the row's 256 bytes, swz(r) = bit 0 of r, plus bits 1-2 of r
+// moved to bits 2-3.  Lanes 8k..8k+7 and 32+8k..32+8k+7 share an LDS cycle;
+// with this map they touch 16 distinct 16-byte slots both when the rows are
+// written and when lane (lrow, lq) reads chunk 4f + lq of row lrow (the
+// operand of fragment f).
+__device__ __forceinline__ int stage_swz(int r) { return (r & 1) | ((r & 6) << 1); }
+__device__ __forceinline__ int stage_chunk(int lrow, int lq) { return lrow ^ ((lq & 2) << 2); }
+__device__ __forceinline__ void stage_transpose(const uint4 (&v)[RT_CHUNK], char* tile, int lrow, int lq,
+                                                uint4 (&t)[RT_CHUNK]) {
+  const int c = stage_chunk(lrow, lq);
+#pragma unroll
+  for (int i = 0; i < RT_CHUNK; ++i) {
+    const int r = 4 * i + lq;
+    *reinterpret_cast<uint4*>(tile + r * 256 + 16 * (c ^ stage_swz(r))) = v[i];
+  }
+  const int sw = stage_swz(lrow);
+#pragma unroll
+  for (int f = 0; f < RT_CHUNK; ++f)
+    t[f] = *reinterpret_cast<const uint4*>(tile + lrow * 256 + 16 * ((4 * f + lq) ^ sw));
+}
 
 // Top-k of one token by a group of 32 lanes (2 tokens per wave, 16 per block):
 // lane r of the group holds experts r, r+32, r+64, ... as 32-bit keys, the
@@ -216,11 +247,20 @@ __device__ __forceinline__ void group_topk(const float* lg, int E, int k, int re
 
 template <typename T, int KS>
 __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
-  __shared__ int s_cnt[RT_WAVES * MAX_GROUPS];
-  __shared__ int s_off[MAX_GROUPS];
-  __shared__ __align__(16) float s_lg[16 * MAX_E];  // wave partials; the tile's logits; later the sort's 16-bit keys
-  __shared__ uint16_t s_pk[16 * MAX_KK];  // sort keys of a single-tile batch
+  // Phase A's per-wave staging tiles share LDS with everything used after it.
+  constexpr int LG_BYTES = 16 * MAX_E * 4;
+  constexpr int CNT_BYTES = RT_WAVES * MAX_GROUPS * 4;
+  constexpr int OFF_BYTES = MAX_GROUPS * 4;
+  constexpr int PK_BYTES = 16 * MAX_KK * 2;
+  constexpr int LATE_BYTES = LG_BYTES + CNT_BYTES + OFF_BYTES + PK_BYTES;
+  constexpr int STAGE_BYTES = RT_WAVES * 2 * RT_TILE;
+  __shared__ __align__(16) char s_raw[STAGE_BYTES > LATE_BYTES ? STAGE_BYTES : LATE_BYTES];
   __shared__ int s_last;              // hand-off flag
+  // wave partials; the tile's logits; later the sort's 16-bit keys
+  float* s_lg = reinterpret_cast<float*>(s_raw);
+  int* s_cnt = reinterpret_cast<int*>(s_raw + LG_BYTES);
+  int* s_off = reinterpret_cast<int*>(s_raw + LG_BYTES + CNT_BYTES);
+  uint16_t* s_pk = reinterpret_cast<uint16_t*>(s_raw + LG_BYTES + CNT_BYTES + OFF_BYTES);  // keys of a single-tile batch
 
   // XCD-aware order: hardware deals blocks to the 8 XCDs round-robin, so
   // logical block b runs on XCD b / (grid / 8) and the blocks of one token
@@ -253,28 +293,40 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       b4[r] = (KS == 1 && a.bias) ? a.bias[min(et * 16 + 4 * lq + r, a.E - 1)] : 0.f;
-    const char* wp = reinterpret_cast<const char*>(a.wg) +
-                     static_cast<size_t>(min(et * 16 + lrow, a.E - 1)) * row_bytes + lq * 16;
-    const char* xp = reinterpret_cast<const char*>(a.x) +
-                     static_cast<size_t>(min(tt * 16 + lrow, a.T - 1)) * row_bytes + lq * 16;
-    // Two register buffers of RT_CHUNK fragments: the next chunk's loads are
-    // in flight while the current one is multiplied.  Addresses are clamped
-    // into the slice, so every load is unconditional; fragments past the
-    // slice end meet zero token fragments.
+    // The lane's rows in the load layout (row 4i + lq of the tile in load i)
+    // and its chunk of each row's 256-byte step.
+    const char* wp[RT_CHUNK];
+    const char* xp[RT_CHUNK];
+#pragma unroll
+    for (int i = 0; i < RT_CHUNK; ++i) {
+      wp[i] = reinterpret_cast<const char*>(a.wg) + static_cast<size_t>(min(et * 16 + 4 * i + lq, a.E - 1)) * row_bytes;
+      xp[i] = reinterpret_cast<const char*>(a.x) + static_cast<size_t>(min(tt * 16 + 4 * i + lq, a.T - 1)) * row_bytes;
+    }
+    const int cbyte = 16 * stage_chunk(lrow, lq);
+    char* wtile = s_raw + wv * 2 * RT_TILE;
+    char* xtile = wtile + RT_TILE;
+    // Two register buffers of RT_CHUNK fragments: the next step's loads are
+    // in flight while the current one is transposed and multiplied.
+    // Addresses are clamped into the slice, so every load is unconditional;
+    // fragments past the slice end meet zero token fragments.
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (f_begin < f_end) {
       uint4 wa[RT_CHUNK], xa[RT_CHUNK], wb[RT_CHUNK], xb[RT_CHUNK];
+      const int b_last = f_end * FRAG_BYTES - 16;
       auto load = [&](int f0, uint4 (&wf)[RT_CHUNK], uint4 (&xf)[RT_CHUNK]) {
+        const int b = min(f0 * FRAG_BYTES + cbyte, b_last);
 #pragma unroll
         for (int i = 0; i < RT_CHUNK; ++i) {
-          const int f = min(f0 + i, f_end - 1);
-          wf[i] = ld16(wp + f * FRAG_BYTES);
-          xf[i] = ld16(xp + f * FRAG_BYTES);
+          wf[i] = ld16(wp[i] + b);
+          xf[i] = ld16(xp[i] + b);
         }
       };
       auto mma = [&](int f0, const uint4 (&wf)[RT_CHUNK], const uint4 (&xf)[RT_CHUNK]) {
+        uint4 wt[RT_CHUNK], xt[RT_CHUNK];
+        stage_transpose(wf, wtile, lrow, lq, wt);
+        stage_transpose(xf, xtile, lrow, lq, xt);
 #pragma unroll
-        for (int i = 0; i < RT_CHUNK; ++i) acc = Elem<T>::mma(wf[i], keep_or_zero(f0 + i < f_end, xf[i]), acc);
+        for (int i = 0; i < RT_CHUNK; ++i) acc = Elem<T>::mma(wt[i], keep_or_zero(f0 + i < f_end, xt[i]), acc);
       };
       load(f_begin, wa, xa);
       for (int f0 = f_begin; f0 < f_end; f0 += 2 * RT_CHUNK) {
@@ -288,6 +340,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     // acc[r] = D[4*lq + r][lrow]: expert et*16 + 4*lq + r, token tt*16 + lrow.
     const int t = tt * 16 + lrow;
     if (kBlockSum) {
+      __syncthreads();  // every wave is done with its staging tiles, which s_lg overlaps
       *reinterpret_cast<f32x4_t*>(s_lg + wv * 256 + 4 * l) = acc;
     } else if (t < a.T) {
       float* dst = (KS == 1) ? a.logits + static_cast<size_t>(t) * a.E
