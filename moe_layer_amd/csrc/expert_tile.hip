@@ -37,6 +37,8 @@
 // one contiguous stretch of that list, so the token tiles that share a
 // weight tile run side by side on one L2 and a group's token rows stay on
 // one or two XCDs.  Every output element is written by exactly one lane.
+#include <type_traits>
+
 #include "common.hpp"
 #include "moe_internal.h"
 
@@ -269,11 +271,11 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
     // are read with the ordinary policy and the later reads find them in L2.
     // Every other weight tile is streamed once, non-temporally.
     const bool keep = n_mt > 1;
-    auto gload = [&](int s, uint4 (&R)[2 * TL_LD]) {
+    auto gload = [&](auto keep_tag, int s, uint4 (&R)[2 * TL_LD]) {
       const int delta = min(0, kbytes - 16 - s * TL_KB - 16 * lc) & ~63;
       const char* wb = wbase + s * TL_KB;
       const char* xb = act + s * TL_KB;
-      if (keep) {
+      if constexpr (decltype(keep_tag)::value) {
 #pragma unroll
         for (int i = 0; i < TL_LD; ++i) R[i] = tl_ldg(wb, woff[i] + delta);
       } else {
@@ -328,44 +330,53 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
     // in between and unconditional stores (a stage past the range is stored
     // and never read), so every path into the loop header leaves the same
     // loads outstanding and the compiler's wait counts stay exact.
-    uint4 R0[2 * TL_LD], R1[2 * TL_LD], R2[2 * TL_LD];
-    gload(sb, R0);
-    gload(min(sb + 1, se - 1), R1);
-    gload(min(sb + 2, se - 1), R2);
-    lstore(sb, R0, s_st[sb & 1]);
-    __syncthreads();
-    int s = sb;
-    for (; s + 2 < se; s += 3) {
-      char* b0 = s_st[s & 1];
-      char* b1 = s_st[(s + 1) & 1];
-      gload(min(s + 3, se - 1), R0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(b0);                     // stage s
-      __builtin_amdgcn_sched_barrier(0);
-      lstore(s + 1, R1, b1);
+    // The load policy is a template parameter of the K loop, fixed per tile:
+    // with a branch around the weight loads inside the loop the compiler
+    // cannot tell which loads are outstanding, and its wait before each
+    // stage's store would drain the next stage's loads as well (one stage
+    // in flight instead of two).
+    auto kloop = [&](auto keep_tag) {
+      uint4 R0[2 * TL_LD], R1[2 * TL_LD], R2[2 * TL_LD];
+      gload(keep_tag, sb, R0);
+      gload(keep_tag, min(sb + 1, se - 1), R1);
+      gload(keep_tag, min(sb + 2, se - 1), R2);
+      lstore(sb, R0, s_st[sb & 1]);
       __syncthreads();
-      gload(min(s + 4, se - 1), R1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(b1);                     // stage s+1
-      __builtin_amdgcn_sched_barrier(0);
-      lstore(s + 2, R2, b0);
-      __syncthreads();
-      gload(min(s + 5, se - 1), R2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(b0);                     // stage s+2
-      __builtin_amdgcn_sched_barrier(0);
-      lstore(s + 3, R0, b1);
-      __syncthreads();
-    }
-    // at most two stages are left: s in LDS, s+1 in R1
-    if (s < se) {
-      compute(s_st[s & 1]);
-      if (s + 1 < se) {
-        lstore(s + 1, R1, s_st[(s + 1) & 1]);
+      int s = sb;
+      for (; s + 2 < se; s += 3) {
+        char* b0 = s_st[s & 1];
+        char* b1 = s_st[(s + 1) & 1];
+        gload(keep_tag, min(s + 3, se - 1), R0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(b0);                     // stage s
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(s + 1, R1, b1);
         __syncthreads();
-        compute(s_st[(s + 1) & 1]);
+        gload(keep_tag, min(s + 4, se - 1), R1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(b1);                     // stage s+1
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(s + 2, R2, b0);
+        __syncthreads();
+        gload(keep_tag, min(s + 5, se - 1), R2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(b0);                     // stage s+2
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(s + 3, R0, b1);
+        __syncthreads();
       }
-    }
+      // at most two stages are left: s in LDS, s+1 in R1
+      if (s < se) {
+        compute(s_st[s & 1]);
+        if (s + 1 < se) {
+          lstore(s + 1, R1, s_st[(s + 1) & 1]);
+          __syncthreads();
+          compute(s_st[(s + 1) & 1]);
+        }
+      }
+    };
+    if (keep) kloop(std::true_type{});
+    else kloop(std::false_type{});
 
     // ---- split tile: store this piece's partial; the last piece of the tile
     // to arrive sums all of them in K order into acc.  Only the 16-row token
