@@ -310,7 +310,51 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     // Addresses are clamped into the slice, so every load is unconditional;
     // fragments past the slice end meet zero token fragments.
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (f_begin < f_end) {
+    // Without block sums the waves of a block take 8 expert tiles of one K
+    // slice, so when the expert tiles come in whole eights they all read the
+    // same 16 token rows: waves 0-3 then load each step's token rows once
+    // (row 4 * wave + lq per lane group) into a block-shared tile, double
+    // buffered (the token halves of waves 0 and 1's own tiles), and every
+    // wave reads its token fragments from there; one barrier per step.  The
+    // buffer a step writes was last read two steps before, behind the
+    // previous step's barrier.
+    bool shared_x = false;
+    if constexpr (!kBlockSum) shared_x = a.n_et % RT_WAVES == 0;
+    if (f_begin < f_end && shared_x) {
+      uint4 wa[RT_CHUNK], wb[RT_CHUNK], xa = make_uint4(0u, 0u, 0u, 0u), xb = xa;
+      const int b_last = f_end * FRAG_BYTES - 16;
+      const int xr = 4 * wv + lq;  // waves 0-3: the token row this lane group loads
+      const char* xrow = reinterpret_cast<const char*>(a.x) + static_cast<size_t>(min(tt * 16 + xr, a.T - 1)) * row_bytes;
+      const int xslot = xr * 256 + 16 * (stage_chunk(lrow, lq) ^ stage_swz(xr));
+      char* sx0 = s_raw + RT_TILE;               // wave 0's token half
+      char* sx1 = s_raw + 3 * RT_TILE;           // wave 1's token half
+      auto load = [&](int f0, uint4 (&wf)[RT_CHUNK], uint4& xf) {
+        const int b = min(f0 * FRAG_BYTES + cbyte, b_last);
+#pragma unroll
+        for (int i = 0; i < RT_CHUNK; ++i) wf[i] = ld16(wp[i] + b);
+        if (wv < 4) xf = ld16(xrow + b);
+      };
+      auto mma = [&](int f0, const uint4 (&wf)[RT_CHUNK], const uint4& xf, char* sx) {
+        if (wv < 4) *reinterpret_cast<uint4*>(sx + xslot) = xf;
+        __syncthreads();
+        uint4 wt[RT_CHUNK], xt[RT_CHUNK];
+        stage_transpose(wf, wtile, lrow, lq, wt);
+        const int sw = stage_swz(lrow);
+#pragma unroll
+        for (int f = 0; f < RT_CHUNK; ++f)
+          xt[f] = *reinterpret_cast<const uint4*>(sx + lrow * 256 + 16 * ((4 * f + lq) ^ sw));
+#pragma unroll
+        for (int i = 0; i < RT_CHUNK; ++i) acc = Elem<T>::mma(wt[i], keep_or_zero(f0 + i < f_end, xt[i]), acc);
+      };
+      load(f_begin, wa, xa);
+      for (int f0 = f_begin; f0 < f_end; f0 += 2 * RT_CHUNK) {
+        load(f0 + RT_CHUNK, wb, xb);
+        mma(f0, wa, xa, sx0);
+        if (f0 + RT_CHUNK >= f_end) break;
+        load(f0 + 2 * RT_CHUNK, wa, xa);
+        mma(f0 + RT_CHUNK, wb, xb, sx1);
+      }
+    } else if (f_begin < f_end) {
       uint4 wa[RT_CHUNK], xa[RT_CHUNK], wb[RT_CHUNK], xb[RT_CHUNK];
       const int b_last = f_end * FRAG_BYTES - 16;
       auto load = [&](int f0, uint4 (&wf)[RT_CHUNK], uint4 (&xf)[RT_CHUNK]) {
