@@ -74,6 +74,7 @@ struct TArgs {
   int m_min;               // groups with more rows than this are computed here ...
   int min_tiles;           // ... when they make at least this many tiles
   int* ctr;                // per-tile arrival counters of split tiles (zero between calls)
+  int* claim;              // TL_XCD whole-tile claim counters, then an exit counter (zero between calls)
   float* part;             // two fp32 partial tiles per block
 };
 
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
   const int wn = wv >> 1;  // weight half of the tile
 
   __shared__ int s_flag;
+  __shared__ int s_claim;
 
   tile_prefix(a, s_tstart, s_off);
   __syncthreads();
@@ -200,8 +202,18 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
   // partial tile's store and reload and a pipeline refill, more than the
   // finer balance gains): XCD x takes the x-th eighth of the tile list and
   // its blocks deal those tiles out in turn, so the token tiles that share
-  // a weight tile run side by side and read it from HBM once.
+  // a weight tile run side by side and read it from HBM once.  When an
+  // eighth holds only a few tiles more than its blocks (at most a quarter
+  // more), each block starts on one of its first tiles and the few left go
+  // to whichever blocks finish first (a claim counter per eighth), so tiles
+  // that run long do not leave the launch waiting on a fixed block's second
+  // tile.  With more left over, dealing them out keeps the token tiles of a
+  // weight tile together, which measured faster; with none, the claims and
+  // their contended counters would only add time.
   const bool whole = 2 * static_cast<long long>(total) >= W;
+  const int xcd = static_cast<int>(blockIdx.x % TL_XCD);
+  const int surplus = (total + TL_XCD - 1) / TL_XCD - per;   // tiles of the largest eighth beyond one per block
+  const bool claim = whole && surplus > 0 && 4 * surplus <= per;
   const int t_lo = static_cast<int>(static_cast<long long>(total) * (blockIdx.x % TL_XCD) / TL_XCD);
   const int t_hi = static_cast<int>(static_cast<long long>(total) * (blockIdx.x % TL_XCD + 1) / TL_XCD);
   const int t_first = t_lo + static_cast<int>(blockIdx.x / TL_XCD);
@@ -221,7 +233,7 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
     const int t = static_cast<int>(q / nst);
     const int sb = static_cast<int>(q - static_cast<long long>(t) * nst);
     const int se = static_cast<int>(min(static_cast<long long>(nst), q1 - static_cast<long long>(t) * nst));
-    q = static_cast<long long>(whole ? t + per : t + 1) * nst;
+    if (!claim) q = static_cast<long long>(whole ? t + per : t + 1) * nst;
     int lo = 0, hi = a.n_groups;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -454,7 +466,16 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
     }
     // the next tile's first stage goes to s_st[0], which the last stage may have used
     __syncthreads();
+    if (claim) {
+      // the next tile of this eighth, or past its end when none is left
+      if (tid == 0) s_claim = atomicAdd(a.claim + xcd, 1);
+      __syncthreads();
+      q = static_cast<long long>(t_lo + per + s_claim) * nst;
+    }
   }
+  // Every block of a claiming launch arrives here after its last claim; the
+  // last one clears the claim counters for the next call.
+  if (claim && last_to_arrive(a.claim + TL_XCD, W, &s_flag) && tid < TL_XCD) a.claim[tid] = 0;
 }
 
 // ---------------------------------------------------------------- host side
@@ -476,10 +497,14 @@ static long long tile_bound(int T, int kk, int n_groups, int m_min, int n_nt) {
   return (pairs / TL_M + big) * n_nt;
 }
 
-static size_t tl_ctr_bytes(int T, int kk, int n_groups, int H, int I) {
+// Split-tile counters (one per tile at most), then the claim counters.
+static long long tl_split_ctrs(int T, int kk, int n_groups, int H, int I) {
   long long n = tile_bound(T, kk, n_groups, TILE_M_MIN, expert_tile_nt(true, H, I));
   const long long d = tile_bound(T, kk, n_groups, TILE_M_MIN, expert_tile_nt(false, H, I));
-  if (d > n) n = d;
+  return d > n ? d : n;
+}
+static size_t tl_ctr_bytes(int T, int kk, int n_groups, int H, int I) {
+  const long long n = tl_split_ctrs(T, kk, n_groups, H, I) + TL_XCD + 1;
   return (static_cast<size_t>(n) * sizeof(int) + 255) & ~static_cast<size_t>(255);
 }
 
@@ -502,6 +527,7 @@ static void tile_launch(TArgs a, int T, void* ws, hipStream_t s) {
   if (grid < TL_XCD) grid = TL_XCD;
   a.min_tiles = tile_min_tiles(a.m_min);
   a.ctr = static_cast<int*>(ws);
+  a.claim = a.ctr + tl_split_ctrs(T, a.kk, a.n_groups, a.H, a.I_loc);
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + tl_ctr_bytes(T, a.kk, a.n_groups, a.H, a.I_loc));
   hipLaunchKernelGGL(expert_tile_kernel<MODE>, dim3(static_cast<unsigned>(grid)), dim3(TL_THREADS), 0, s, a);
 }

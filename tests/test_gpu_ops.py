@@ -413,6 +413,32 @@ def test_repeated_runs_are_bit_identical():
         assert np.array_equal(va, vb), key
 
 
+# The LDS-tiled kernels hand the few tiles left after one tile per block to
+# whichever blocks finish first, through claim counters in the workspace that
+# the last block clears.  1950 tokens over 16 experts (195-278 rows each) make
+# 576 up tiles, 8 more per XCD than its 64 blocks on MI355X, so the up launch
+# claims.  Two passes on one set of buffers (the workspace included) must
+# both match the oracle: counters left set would drop tiles in the second.
+def test_tile_claims_leave_workspace_reusable():
+    import torch
+
+    import gpu_helpers as gh
+    import moe_layer_amd
+    cfg = small(H=1024, E=16, k=2, I=1024, T=1950)
+    d = make_layer_inputs(cfg, 1950, routing="uniform", seed=31)
+    x, wg, b = gh.to_dev(d["x"]), gh.to_dev(d["w_gate"]), gh.to_dev(d["gate_bias"])
+    w13, w2 = gh.to_dev(d["w13"]), gh.to_dev(d["w2"])
+    print("[case] tile claims, two passes on one workspace", flush=True)
+    bufs = None
+    for _ in range(2):
+        bufs = moe_layer_amd.moe_layer_forward(x, wg, b, w13, w2, cfg.k, cfg.renorm, bufs=bufs)
+        torch.cuda.synchronize()
+        g = {name: gh.from_dev(getattr(bufs, name)) for name in
+             ("logits", "topk_ids", "topk_w", "counts", "offsets", "sorted_pair", "pair_pos", "a", "y_pair", "y")}
+        assert g["counts"].min() > 128, g["counts"]   # every group past one 128-row token tile
+        gh.check_layer(d, cfg, g)
+
+
 def test_graph_replay_matches_eager():
     import torch
 
