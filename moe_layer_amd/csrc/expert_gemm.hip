@@ -599,12 +599,14 @@ static void launch_tm(XArgs a, int nt, int sub, hipStream_t s) {
 
 // Token tiles per pass of the short-row down kernel, from the mean rows per
 // group: it holds a pass's token fragments in registers and takes every
-// group, so passes of 64 and 128 rows serve the larger batches.
+// group, so passes of 64 and 128 rows serve the larger batches.  Groups of
+// about 64 rows take one 128-row pass rather than one or two of 64 (TP
+// B = 1024: 84.5 -> 64.8 us); at 32 rows both are alike.
 static int short_nt(int T, int kk, int n_groups) {
   const double mean = static_cast<double>(T) * kk / n_groups;
   if (T <= 16 || mean <= 12.0) return 1;
   if (mean <= 24.0) return 2;
-  return mean <= 64.0 ? 4 : 8;
+  return mean <= 40.0 ? 4 : 8;
 }
 
 // Whether the down-projection of these shapes runs entirely in the short-row
