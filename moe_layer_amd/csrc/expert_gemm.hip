@@ -461,11 +461,13 @@ __global__ __launch_bounds__(XW_WAVES * WAVE) void expert_wave_kernel(XArgs a) {
 static int elem_bytes_x(int dtype) { return dtype == 1 ? 2 : 4; }
 
 // Token tiles from the mean rows per group (exact for the full and TP views;
-// an over-estimate for an EP share): two from 8 rows on (groups of 8-16 rows
-// vary enough that many need a second 16-row pass, which then re-reads the
-// weights: Qwen3-30B T = 128 down 86.5 -> 76.8 us, T = 192 step 294 -> 248
-// us, TP Zipf B = 160 125 -> 108 us; at 4 rows two tiles cost 5 us); four for
-// batches of 384..767 tokens with more than 24 (groups of 33..64 rows then
+// an over-estimate, by the rank count, for an EP share): two above 12, and
+// from 64 tokens on already from 8 rows (groups of 8-16 rows vary enough that
+// many need a second 16-row pass, which then re-reads the weights: Qwen3-30B
+// T = 128 down 86.5 -> 76.8 us, T = 192 step 294 -> 248 us, TP Zipf B = 160
+// 125 -> 108 us; at 4 rows two tiles cost 5 us, and below 64 tokens an EP
+// share's estimate of 8 means about one row, where two tiles cost 8 us); four
+// for batches of 384..767 tokens with more than 24 (groups of 33..64 rows then
 // take one pass instead of two, or the LDS-tiled kernel, which is
 // latency-bound with few tiles).  Four tiles need one wave per SIMD and
 // compute more per chunk, so they lose wherever groups hold 32 rows or fewer.
@@ -473,7 +475,7 @@ static int pick_nt(int T, int kk, int n_groups) {
   const double mean = static_cast<double>(T) * kk / n_groups;
   if (T <= 16) return 1;
   if (T >= 384 && T < 768 && mean > 24.0) return 4;
-  return mean > 7.0 ? 2 : 1;
+  return (mean > 12.0 || (T >= 64 && mean > 7.0)) ? 2 : 1;
 }
 
 int expert_tile_m_min(int T, int kk, int n_groups) {
