@@ -608,14 +608,14 @@ def ingest_counters(fetch_csv, write_csv, name, T, routing, command):
     c.setdefault("fetch_scale", 1.9994)
     c.setdefault("write_scale", 0.9997)
     entries = [e for e in c.get("entries", []) if (e.get("workload"), e.get("T"), e.get("routing")) != (name, T, routing)]
-    entries.append({"workload": name, "T": T, "routing": routing, "kernel": "moe_expert_up (expert_{wave,coop}_kernel<bf16, UP, ...>)",
-                    "source_sha": kernel_source_sha(), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
-                    "dispatches": min(nf, nw), "commands": command})
-    c["entries"] = sorted(entries, key=lambda e: (e["workload"], e["routing"], e["T"]))
+    new = {"workload": name, "T": T, "routing": routing, "kernel": "moe_expert_up (expert_{wave,coop}_kernel<bf16, UP, ...>)",
+           "source_sha": kernel_source_sha(), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+           "dispatches": min(nf, nw), "commands": command}
+    c["entries"] = sorted(entries + [new], key=lambda e: (e["workload"], e["routing"], e["T"]))
     with open(PROFILE_COUNTERS, "w") as f:
         json.dump(c, f, indent=1)
         f.write("\n")
-    print(json.dumps(c["entries"][-1]))
+    print(json.dumps(new))
 
 
 def cpu_baseline(wl, budget_s=10.0):
