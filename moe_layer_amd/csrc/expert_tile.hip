@@ -56,6 +56,8 @@ constexpr int TL_XCD = 8;
 constexpr int TL_MIN_ST = 8;                   // stages per block at least
 constexpr int TL_MAX_GRID = 512;               // blocks of a launch at most
 constexpr int TL_PART_FLOATS = TL_M * TL_N;    // fp32 partial tile
+constexpr int TL_MAX_PIECES = 2;               // pieces a leftover tile is cut into at most
+constexpr int TL_PIECE_ST = 16;                // stages per piece of a leftover tile at least
 
 enum TMode { TMODE_UP = 0, TMODE_DOWN = 1 };
 
@@ -74,8 +76,9 @@ struct TArgs {
   int m_min;               // groups with more rows than this are computed here ...
   int min_tiles;           // ... when they make at least this many tiles
   int* ctr;                // per-tile arrival counters of split tiles (zero between calls)
-  int* claim;              // TL_XCD whole-tile claim counters, then an exit counter (zero between calls)
+  int* claim;              // TL_XCD claim counters, then an exit counter (zero between calls)
   float* part;             // two fp32 partial tiles per block
+  int max_pieces;          // leftover tiles are cut into at most this many pieces along K
 };
 
 // Byte offset of 16-byte chunk c (0..7) of row r inside an operand region.
@@ -207,13 +210,21 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
   // more), each block starts on one of its first tiles and the few left go
   // to whichever blocks finish first (a claim counter per eighth), so tiles
   // that run long do not leave the launch waiting on a fixed block's second
-  // tile.  With more left over, dealing them out keeps the token tiles of a
-  // weight tile together, which measured faster; with none, the claims and
-  // their contended counters would only add time.
+  // tile.  Each leftover tile is cut along K into S <= TL_MAX_PIECES pieces
+  // of at least TL_PIECE_ST stages, S chosen so that all pieces of an eighth
+  // can run at once on its blocks: a claim takes one piece, and the last
+  // piece of a tile to finish sums the pieces' partials in K order.  The
+  // leftover then costs about a piece's time after the first tiles instead
+  // of a tile's.  (More or shorter pieces measured slower: each adds a
+  // partial tile's store and reload and a pipeline refill.)
+  // With more left over, dealing them out keeps the token tiles of a weight
+  // tile together, which measured faster; with none, the claims and their
+  // contended counters would only add time.
   const bool whole = 2 * static_cast<long long>(total) >= W;
   const int xcd = static_cast<int>(blockIdx.x % TL_XCD);
   const int surplus = (total + TL_XCD - 1) / TL_XCD - per;   // tiles of the largest eighth beyond one per block
   const bool claim = whole && surplus > 0 && 4 * surplus <= per;
+  const int n_pc = claim ? max(1, min(min(per / max(surplus, 1), nst / TL_PIECE_ST), a.max_pieces)) : 1;
   const int t_lo = static_cast<int>(static_cast<long long>(total) * (blockIdx.x % TL_XCD) / TL_XCD);
   const int t_hi = static_cast<int>(static_cast<long long>(total) * (blockIdx.x % TL_XCD + 1) / TL_XCD);
   const int t_first = t_lo + static_cast<int>(blockIdx.x / TL_XCD);
@@ -228,12 +239,32 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
 #pragma unroll
   for (int i = 0; i < TL_LD; ++i) sw[i] = tl_swz(lrow + 32 * i, lc);
 
-  for (long long q = q0; q < q1;) {
+  // claimable pieces of this eighth: its tiles beyond one per block, n_pc each
+  const int n_claims = claim ? (t_hi - t_lo - per) * n_pc : 0;
+  long long q = q0;
+  int c = -1;   // claim of the current unit (claiming launches; -1: the block's first tile)
+  for (;;) {
     // ---- this block's piece of tile t: stages [sb, se) (block-uniform)
-    const int t = static_cast<int>(q / nst);
-    const int sb = static_cast<int>(q - static_cast<long long>(t) * nst);
-    const int se = static_cast<int>(min(static_cast<long long>(nst), q1 - static_cast<long long>(t) * nst));
-    if (!claim) q = static_cast<long long>(whole ? t + per : t + 1) * nst;
+    int t, sb, se;
+    if (claim) {
+      if (c < 0) {
+        t = t_first;   // < t_lo + per <= t_hi
+        sb = 0;
+        se = nst;
+      } else {
+        if (c >= n_claims) break;
+        t = t_lo + per + c / n_pc;
+        const int j = c - (c / n_pc) * n_pc;
+        sb = j * nst / n_pc;
+        se = (j + 1) * nst / n_pc;
+      }
+    } else {
+      if (q >= q1) break;
+      t = static_cast<int>(q / nst);
+      sb = static_cast<int>(q - static_cast<long long>(t) * nst);
+      se = static_cast<int>(min(static_cast<long long>(nst), q1 - static_cast<long long>(t) * nst));
+      q = static_cast<long long>(whole ? t + per : t + 1) * nst;
+    }
     int lo = 0, hi = a.n_groups;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -392,13 +423,24 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
 
     // ---- split tile: store this piece's partial; the last piece of the tile
     // to arrive sums all of them in K order into acc.  Only the 16-row token
-    // tiles that hold rows of the group are kept.
+    // tiles that hold rows of the group are kept.  Stream-K pieces belong to
+    // blocks wa..wb (two partial slots per block); a claimed piece j of
+    // leftover tile u of an eighth has slot xcd * per + u * n_pc + j.
+    bool epilogue = true;
     if (sb != 0 || se != nst) {
-      const long long qa = static_cast<long long>(t) * nst;
-      const int wa = tl_owner(qa, Q, W);
-      const int wb = tl_owner(qa + nst - 1, Q, W);
+      int wa, wb;
+      float* mine;
+      if (claim) {
+        wa = xcd * per + (t - t_lo - per) * n_pc;
+        wb = wa + n_pc - 1;
+        mine = a.part + static_cast<size_t>(xcd * per + c) * TL_PART_FLOATS;
+      } else {
+        const long long qa = static_cast<long long>(t) * nst;
+        wa = tl_owner(qa, Q, W);
+        wb = tl_owner(qa + nst - 1, Q, W);
+        mine = tl_slot(a.part, w, t, nst, Q, W);
+      }
       const int l_rows = m - m0 - 64 * wm;   // valid token rows of this wave's half
-      float* mine = tl_slot(a.part, w, t, nst, Q, W);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -408,9 +450,9 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
             st_agent(p, (static_cast<uint64_t>(__float_as_uint(acc[i][j][1])) << 32) | __float_as_uint(acc[i][j][0]));
             st_agent(p + 1, (static_cast<uint64_t>(__float_as_uint(acc[i][j][3])) << 32) | __float_as_uint(acc[i][j][2]));
           }
-      if (!last_to_arrive(a.ctr + t, wb - wa + 1, &s_flag)) continue;  // block-uniform
-      for (int v = wa; v <= wb; ++v) {
-        const float* src = tl_slot(a.part, v, t, nst, Q, W);
+      epilogue = last_to_arrive(a.ctr + t, wb - wa + 1, &s_flag);  // block-uniform
+      for (int v = wa; epilogue && v <= wb; ++v) {
+        const float* src = claim ? a.part + static_cast<size_t>(v) * TL_PART_FLOATS : tl_slot(a.part, v, t, nst, Q, W);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -427,7 +469,8 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
     }
 
     // ---- epilogue: acc[i][j][r] = D[weight row 4*lq + r of tile i][token row lr of tile j]
-    if (MODE == TMODE_UP) {
+    if (!epilogue) {
+    } else if (MODE == TMODE_UP) {
       uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -467,10 +510,10 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
     // the next tile's first stage goes to s_st[0], which the last stage may have used
     __syncthreads();
     if (claim) {
-      // the next tile of this eighth, or past its end when none is left
+      // the next piece of this eighth, or past its end when none is left
       if (tid == 0) s_claim = atomicAdd(a.claim + xcd, 1);
       __syncthreads();
-      q = static_cast<long long>(t_lo + per + s_claim) * nst;
+      c = s_claim;
     }
   }
   // Every block of a claiming launch arrives here after its last claim; the
@@ -529,6 +572,7 @@ static void tile_launch(TArgs a, int T, void* ws, hipStream_t s) {
   a.ctr = static_cast<int*>(ws);
   a.claim = a.ctr + tl_split_ctrs(T, a.kk, a.n_groups, a.H, a.I_loc);
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + tl_ctr_bytes(T, a.kk, a.n_groups, a.H, a.I_loc));
+  a.max_pieces = TL_MAX_PIECES;
   hipLaunchKernelGGL(expert_tile_kernel<MODE>, dim3(static_cast<unsigned>(grid)), dim3(TL_THREADS), 0, s, a);
 }
 

@@ -414,21 +414,25 @@ def test_repeated_runs_are_bit_identical():
 
 
 # The LDS-tiled kernels hand the few tiles left after one tile per block to
-# whichever blocks finish first, through claim counters in the workspace that
-# the last block clears.  1950 tokens over 16 experts (195-278 rows each) make
-# 576 up tiles, 8 more per XCD than its 64 blocks on MI355X, so the up launch
-# claims.  Two passes on one set of buffers (the workspace included) must
-# both match the oracle: counters left set would drop tiles in the second.
-def test_tile_claims_leave_workspace_reusable():
+# whichever blocks finish first, cut along K into pieces, through claim
+# counters in the workspace that the last block clears; the last piece of a
+# tile to finish sums the pieces.  1950 tokens over 16 experts (195-278 rows
+# each) make 576 up tiles, 8 more per XCD than its 64 blocks on MI355X,
+# so the up launch claims: with H = 1024 (16 K stages) whole leftover tiles,
+# with H = 4096 (64 stages) halves of them.  Two passes on one set of
+# buffers (the workspace included) must both match the oracle: counters left
+# set would drop tiles in the second.
+@pytest.mark.parametrize("H", [1024, 4096])
+def test_tile_claims_leave_workspace_reusable(H):
     import torch
 
     import gpu_helpers as gh
     import moe_layer_amd
-    cfg = small(H=1024, E=16, k=2, I=1024, T=1950)
-    d = make_layer_inputs(cfg, 1950, routing="uniform", seed=31)
+    cfg = small(H=H, E=16, k=2, I=1024, T=1950)
+    d = make_layer_inputs(cfg, 1950, routing="uniform", seed=31 if H == 1024 else 32)  # no near-ties
     x, wg, b = gh.to_dev(d["x"]), gh.to_dev(d["w_gate"]), gh.to_dev(d["gate_bias"])
     w13, w2 = gh.to_dev(d["w13"]), gh.to_dev(d["w2"])
-    print("[case] tile claims, two passes on one workspace", flush=True)
+    print(f"[case] tile claims, two passes on one workspace, H={H}", flush=True)
     bufs = None
     for _ in range(2):
         bufs = moe_layer_amd.moe_layer_forward(x, wg, b, w13, w2, cfg.k, cfg.renorm, bufs=bufs)
