@@ -443,20 +443,29 @@ def test_tile_claims_leave_workspace_reusable(H):
         gh.check_layer(d, cfg, g)
 
 
-def test_graph_replay_matches_eager():
+# T = 600 under Zipf routing (groups of 10-556 rows) runs both expert kernels
+# of each projection in the graph: the LDS-tiled one (claims, split tiles)
+# and the wave-streaming one, each checked against the oracle first.
+@pytest.mark.parametrize("T,E,k,H,I,routing", [(64, 32, 4, 256, 128, "uniform"), (600, 16, 4, 512, 512, "zipf")])
+def test_graph_replay_matches_eager(T, E, k, H, I, routing):
     import torch
 
     import gpu_helpers as gh
     import moe_layer_amd
-    cfg = small(E=32, k=4, T=64)
-    d = make_layer_inputs(cfg, 64, seed=8)
+    cfg = small(E=E, k=k, T=T, H=H, I=I)
+    d = make_layer_inputs(cfg, T, routing=routing, seed=8 if T == 64 else 9)
     x, wg, b = gh.to_dev(d["x"]), gh.to_dev(d["w_gate"]), gh.to_dev(d["gate_bias"])
     w13, w2 = gh.to_dev(d["w13"]), gh.to_dev(d["w2"])
-    print("[case] graph replay", flush=True)
+    print(f"[case] graph replay T={T} {routing}", flush=True)
     eager = moe_layer_amd.moe_layer_forward(x, wg, b, w13, w2, cfg.k, cfg.renorm)
     torch.cuda.synchronize()
     want = gh.from_dev(eager.y).copy()
-    bufs = moe_layer_amd.MoeLayerBuffers.allocate(64, cfg.H, cfg.E, cfg.k, cfg.E, cfg.I, torch.bfloat16)
+    if T > 256:
+        g = {name: gh.from_dev(getattr(eager, name)) for name in
+             ("logits", "topk_ids", "topk_w", "counts", "offsets", "sorted_pair", "pair_pos", "a", "y_pair", "y")}
+        assert g["counts"].min() <= 32 < g["counts"].max() // 4   # both kernels of a projection have groups
+        gh.check_layer(d, cfg, g)
+    bufs = moe_layer_amd.MoeLayerBuffers.allocate(T, cfg.H, cfg.E, cfg.k, cfg.E, cfg.I, torch.bfloat16)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
