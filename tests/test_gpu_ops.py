@@ -487,14 +487,19 @@ def test_graph_replay_matches_eager(T, E, k, H, I, routing):
 @pytest.mark.parametrize("T,E,k,n_shared,H", [(3000, 64, 8, 0, 256), (8, 128, 8, 0, 4096),
                                                (40, 64, 6, 2, 2048), (1, 128, 8, 0, 4096),
                                                (13, 128, 8, 2, 4096), (16, 64, 6, 2, 2048),
-                                               (17, 128, 8, 0, 4096), (9000, 64, 8, 0, 256)])
+                                               (17, 128, 8, 0, 4096), (9000, 64, 8, 0, 256),
+                                               (1100, 128, 8, 0, 1024), (1030, 128, 2, 1, 1024),
+                                               (1040, 256, 4, 0, 2048)])
 def test_fused_route_matches_two_calls_and_leaves_workspace_zero(T, E, k, n_shared, H):
     """One launch (routing + sort) against moe_route then moe_permute; the
     3000-token case has more pairs than the sort stages in LDS, and 9000
     tokens (72 000 pairs) route and then sort in the three-launch permute.  At H = 2048
     and 4096 the gate GEMM runs 8 or 16 K slices summed per block; T <= 16
     (one token tile, T = 1 and 13 ragged) sorts in the top-k block from LDS,
-    and T = 17 hands a one-token second tile to the sorting block."""
+    and T = 17 hands a one-token second tile to the sorting block.  T = 1100
+    and 1030 end in a ragged token tile (1030 x 3 pairs sort in the routing
+    launch, with a shared slot); E = 256 takes two blocks per K slice of a
+    token tile.  The logits are checked against the fp64 oracle too."""
     import torch
 
     import gpu_helpers as gh
@@ -526,6 +531,9 @@ def test_fused_route_matches_two_calls_and_leaves_workspace_zero(T, E, k, n_shar
     for key in outs[0]:
         assert np.array_equal(outs[0][key], outs[1][key]), key
         assert np.array_equal(outs[0][key], outs[2][key]), key
+    lg_ref = oracle.gate_logits(d["x"], d["w_gate"], d["gate_bias"])
+    lerr = np.abs(outs[0]["logits"].astype(np.float64) - lg_ref).max()
+    assert lerr <= gh.LOGIT_REL * np.abs(lg_ref).max(), f"logits max err {lerr:.3e}"
     ids_ref, w_ref = oracle.route(outs[0]["logits"].astype(np.float64), k, False, n_shared)
     assert np.array_equal(outs[0]["topk_ids"], ids_ref)
     assert np.abs(outs[0]["topk_w"] - w_ref).max() <= 1e-5
