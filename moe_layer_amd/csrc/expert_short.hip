@@ -37,6 +37,7 @@ namespace {
 
 constexpr int SH_WAVES = 4;  // waves per block (one block per CU)
 constexpr int SH_RING = 4;   // weight tiles a wave holds: the one it multiplies and the next three
+constexpr long long SH_KEEP_BYTES = 32LL << 20;  // weights of multi-pass groups read with the ordinary policy, at most (the chip's L2)
 
 // One step of the sequence, decoded (wave-uniform): group, weight tile j,
 // the group's first sorted row, and the pass's rows [t0, m_end).
@@ -68,8 +69,9 @@ __device__ __forceinline__ SStep sh_decode(const XArgs& a, const int* s_istart, 
 template <int KF>
 constexpr int sh_pitch() { return KF * FRAG_BYTES + 16; }  // LDS row pitch of the transpose tile
 
-// The stream of one wave, after the step table is built (NT token tiles per pass).
-template <int KF, int NT>
+// The stream of one wave, after the step table is built (NT token tiles per
+// pass; KEEP: weights read with the ordinary policy instead of streamed).
+template <int KF, int NT, bool KEEP>
 __device__ __forceinline__ void short_body(const XArgs& a, const int* s_istart, const int* s_off, char* tile, int wv) {
   constexpr int RB = KF * FRAG_BYTES;  // bytes of a weight row and of an activation row
   constexpr int PITCH = sh_pitch<KF>();
@@ -113,7 +115,10 @@ __device__ __forceinline__ void short_body(const XArgs& a, const int* s_istart, 
   auto load_w = [&](const SStep& d, uint4 (&r)[KF]) {
     const char* b = wtile(d);
 #pragma unroll
-    for (int i = 0; i < KF; ++i) r[i] = ldg_nt(b + 1024 * i, static_cast<uint32_t>(16 * l));
+    for (int i = 0; i < KF; ++i) {
+      if constexpr (KEEP) r[i] = ldg(b + 1024 * i, static_cast<uint32_t>(16 * l));
+      else r[i] = ldg_nt(b + 1024 * i, static_cast<uint32_t>(16 * l));
+    }
   };
   auto load_x = [&](const SStep& d, uint4 (&x)[NT][KF]) {
 #pragma unroll
@@ -205,20 +210,59 @@ template <int KF, int NT>
 __global__ __launch_bounds__(SH_WAVES * WAVE) void expert_short_kernel(XArgs a) {
   __shared__ int s_istart[MAX_GROUPS + 1];
   __shared__ int s_off[MAX_GROUPS + 1];
-  __shared__ int s_ntx;
+  __shared__ int s_ntx, s_multi[2];
   __shared__ __attribute__((aligned(16))) char s_wt[SH_WAVES][16 * sh_pitch<KF>()];
 
   const int wv = uni(threadIdx.x / WAVE);
+  const int l = lane_id();
   // steps per group: its passes x H / 16 tiles (none for groups the tile
   // kernels take); a kernel built for four token tiles runs two when no
   // group holds more than 32 rows
   item_prefix<NT>(a.offsets, a.n_groups, a.n_tiles, a.tile_nt, a.tile_min, a.tile_m_min, s_istart, s_off, &s_ntx);
+  if (wv == SH_WAVES - 1) {
+    // groups with more than one pass, for passes of 16 * NT rows and (the
+    // body a four-tile kernel may run instead) of 32
+    int n0 = 0, n1 = 0;
+    for (int g = l; g < a.n_groups; g += WAVE) {
+      const int m = a.offsets[g + 1] - a.offsets[g];
+      n0 += m > pass_rows<NT>(m);
+      n1 += m > pass_rows<2>(m);
+    }
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+      n0 += __shfl_xor(n0, d, WAVE);
+      n1 += __shfl_xor(n1, d, WAVE);
+    }
+    if (l == 0) {
+      s_multi[0] = n0;
+      s_multi[1] = n1;
+    }
+  }
   __syncthreads();  // the only barrier; waves are independent from here on
+  // When the groups with several passes hold at most SH_KEEP_BYTES of weights
+  // (a few hot experts), every weight tile is read with the ordinary policy:
+  // the passes of a group run side by side on one XCD (the waves' ranges are
+  // contiguous), so the later ones find the tiles in L2.  Qwen3-235B TP share
+  // under Zipf routing: B = 64 21.0 -> 19.5 us, B = 256 44.1 -> 34.8, B = 2048
+  // 120.8 -> 114.0.  With more such groups (uniform routing, B = 2048: about
+  // 64 of 1.5 MB) the temporal loads crowd L2 and the launch got slower (110
+  // -> 124 us), so those launches stream, as do launches of one pass per
+  // group.
+  const bool four = NT == 4 && uni(s_ntx) == 4;
+  const long long group_bytes = static_cast<long long>(a.n_tiles) * 16 * KF * FRAG_BYTES;
+  const int n_multi = uni(NT == 4 && !four ? s_multi[1] : s_multi[0]);
+  const bool keep = n_multi > 0 && n_multi * group_bytes <= SH_KEEP_BYTES;
   if constexpr (NT == 4) {
-    if (uni(s_ntx) == 4) short_body<KF, 4>(a, s_istart, s_off, s_wt[wv], wv);
-    else short_body<KF, 2>(a, s_istart, s_off, s_wt[wv], wv);
+    if (four) {
+      if (keep) short_body<KF, 4, true>(a, s_istart, s_off, s_wt[wv], wv);
+      else short_body<KF, 4, false>(a, s_istart, s_off, s_wt[wv], wv);
+    } else {
+      if (keep) short_body<KF, 2, true>(a, s_istart, s_off, s_wt[wv], wv);
+      else short_body<KF, 2, false>(a, s_istart, s_off, s_wt[wv], wv);
+    }
   } else {
-    short_body<KF, NT>(a, s_istart, s_off, s_wt[wv], wv);
+    if (keep) short_body<KF, NT, true>(a, s_istart, s_off, s_wt[wv], wv);
+    else short_body<KF, NT, false>(a, s_istart, s_off, s_wt[wv], wv);
   }
 }
 
