@@ -76,7 +76,7 @@ struct TArgs {
   int m_min;               // groups with more rows than this are computed here ...
   int min_tiles;           // ... when they make at least this many tiles
   int* ctr;                // per-tile arrival counters of split tiles (zero between calls)
-  int* claim;              // TL_XCD claim counters, then an exit counter (zero between calls)
+  int* claim;              // the launch's claim counter, then an exit counter (zero between calls)
   float* part;             // two fp32 partial tiles per block
   int max_pieces;          // leftover tiles are cut into at most this many pieces along K
 };
@@ -208,20 +208,22 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
   // a weight tile run side by side and read it from HBM once.  When an
   // eighth holds only a few tiles more than its blocks (at most a quarter
   // more), each block starts on one of its first tiles and the few left go
-  // to whichever blocks finish first (a claim counter per eighth), so tiles
-  // that run long do not leave the launch waiting on a fixed block's second
-  // tile.  Each leftover tile is cut along K into S <= TL_MAX_PIECES pieces
-  // of at least TL_PIECE_ST stages, S chosen so that all pieces of an eighth
-  // can run at once on its blocks: a claim takes one piece, and the last
-  // piece of a tile to finish sums the pieces' partials in K order.  The
-  // leftover then costs about a piece's time after the first tiles instead
-  // of a tile's.  (More or shorter pieces measured slower: each adds a
-  // partial tile's store and reload and a pipeline refill.)
+  // to whichever blocks finish first, so tiles that run long do not leave
+  // the launch waiting on a fixed block's second tile.  Each leftover tile is
+  // cut along K into S <= TL_MAX_PIECES pieces of at least TL_PIECE_ST
+  // stages, S chosen so that all pieces of an eighth could run at once on its
+  // blocks.  The pieces of all eighths form one list (eighth by eighth, tile
+  // by tile, in K order) handed out by one counter, so a block of an XCD that
+  // finishes early also takes pieces of the other XCDs' leftovers (one
+  // counter per eighth left EP B = 2048 up 9 us longer); the last piece of a
+  // tile to finish sums the pieces' partials in K order.  The leftover then
+  // costs about a piece's time after the first tiles instead of a tile's.
+  // (More or shorter pieces measured slower: each adds a partial tile's store
+  // and reload and a pipeline refill.)
   // With more left over, dealing them out keeps the token tiles of a weight
   // tile together, which measured faster; with none, the claims and their
   // contended counters would only add time.
   const bool whole = 2 * static_cast<long long>(total) >= W;
-  const int xcd = static_cast<int>(blockIdx.x % TL_XCD);
   const int surplus = (total + TL_XCD - 1) / TL_XCD - per;   // tiles of the largest eighth beyond one per block
   const bool claim = whole && surplus > 0 && 4 * surplus <= per;
   const int n_pc = claim ? max(1, min(min(per / max(surplus, 1), nst / TL_PIECE_ST), a.max_pieces)) : 1;
@@ -239,13 +241,14 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
 #pragma unroll
   for (int i = 0; i < TL_LD; ++i) sw[i] = tl_swz(lrow + 32 * i, lc);
 
-  // claimable pieces of this eighth: its tiles beyond one per block, n_pc each
-  const int n_claims = claim ? (t_hi - t_lo - per) * n_pc : 0;
+  // claimable pieces: the tiles of each eighth beyond one per block, n_pc each
+  const int n_claims = claim ? (total - W) * n_pc : 0;
   long long q = q0;
   int c = -1;   // claim of the current unit (claiming launches; -1: the block's first tile)
   for (;;) {
     // ---- this block's piece of tile t: stages [sb, se) (block-uniform)
     int t, sb, se;
+    int pj = 0;  // piece of a claimed leftover tile
     if (claim) {
       if (c < 0) {
         t = t_first;   // < t_lo + per <= t_hi
@@ -253,10 +256,19 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
         se = nst;
       } else {
         if (c >= n_claims) break;
-        t = t_lo + per + c / n_pc;
-        const int j = c - (c / n_pc) * n_pc;
-        sb = j * nst / n_pc;
-        se = (j + 1) * nst / n_pc;
+        // the eighth whose leftover pieces hold claim c (block-uniform)
+        int base = 0, x = 0, nx = 0;
+        for (; x < TL_XCD - 1; ++x) {
+          nx = (static_cast<int>(static_cast<long long>(total) * (x + 1) / TL_XCD) -
+                static_cast<int>(static_cast<long long>(total) * x / TL_XCD) - per) * n_pc;
+          if (c < base + nx) break;
+          base += nx;
+        }
+        const int u = (c - base) / n_pc;
+        pj = c - base - u * n_pc;
+        t = static_cast<int>(static_cast<long long>(total) * x / TL_XCD) + per + u;
+        sb = pj * nst / n_pc;
+        se = (pj + 1) * nst / n_pc;
       }
     } else {
       if (q >= q1) break;
@@ -424,16 +436,17 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
     // ---- split tile: store this piece's partial; the last piece of the tile
     // to arrive sums all of them in K order into acc.  Only the 16-row token
     // tiles that hold rows of the group are kept.  Stream-K pieces belong to
-    // blocks wa..wb (two partial slots per block); a claimed piece j of
-    // leftover tile u of an eighth has slot xcd * per + u * n_pc + j.
+    // blocks wa..wb (two partial slots per block); a claimed piece has the
+    // slot of its claim number (< W), so piece pj of a tile is pj slots after
+    // the tile's first.
     bool epilogue = true;
     if (sb != 0 || se != nst) {
       int wa, wb;
       float* mine;
       if (claim) {
-        wa = xcd * per + (t - t_lo - per) * n_pc;
+        wa = c - pj;
         wb = wa + n_pc - 1;
-        mine = a.part + static_cast<size_t>(xcd * per + c) * TL_PART_FLOATS;
+        mine = a.part + static_cast<size_t>(c) * TL_PART_FLOATS;
       } else {
         const long long qa = static_cast<long long>(t) * nst;
         wa = tl_owner(qa, Q, W);
@@ -469,8 +482,7 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
     }
 
     // ---- epilogue: acc[i][j][r] = D[weight row 4*lq + r of tile i][token row lr of tile j]
-    if (!epilogue) {
-    } else if (MODE == TMODE_UP) {
+    if (epilogue && MODE == TMODE_UP) {
       uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -491,7 +503,7 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
           }
         }
       }
-    } else {
+    } else if (epilogue) {
       uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -510,15 +522,15 @@ __global__ __launch_bounds__(TL_THREADS, 2) void expert_tile_kernel(TArgs a) {
     // the next tile's first stage goes to s_st[0], which the last stage may have used
     __syncthreads();
     if (claim) {
-      // the next piece of this eighth, or past its end when none is left
-      if (tid == 0) s_claim = atomicAdd(a.claim + xcd, 1);
+      // the next piece, or past the end of the list when none is left
+      if (tid == 0) s_claim = atomicAdd(a.claim, 1);
       __syncthreads();
       c = s_claim;
     }
   }
   // Every block of a claiming launch arrives here after its last claim; the
-  // last one clears the claim counters for the next call.
-  if (claim && last_to_arrive(a.claim + TL_XCD, W, &s_flag) && tid < TL_XCD) a.claim[tid] = 0;
+  // last one clears the claim counter for the next call.
+  if (claim && last_to_arrive(a.claim + 1, W, &s_flag) && tid == 0) a.claim[0] = 0;
 }
 
 // ---------------------------------------------------------------- host side
@@ -547,7 +559,7 @@ static long long tl_split_ctrs(int T, int kk, int n_groups, int H, int I) {
   return d > n ? d : n;
 }
 static size_t tl_ctr_bytes(int T, int kk, int n_groups, int H, int I) {
-  const long long n = tl_split_ctrs(T, kk, n_groups, H, I) + TL_XCD + 1;
+  const long long n = tl_split_ctrs(T, kk, n_groups, H, I) + 2;
   return (static_cast<size_t>(n) * sizeof(int) + 255) & ~static_cast<size_t>(255);
 }
 

@@ -414,8 +414,8 @@ def test_repeated_runs_are_bit_identical():
 
 
 # The LDS-tiled kernels hand the few tiles left after one tile per block to
-# whichever blocks finish first, cut along K into pieces, through claim
-# counters in the workspace that the last block clears; the last piece of a
+# whichever blocks finish first, cut along K into pieces, through a claim
+# counter in the workspace that the last block clears; the last piece of a
 # tile to finish sums the pieces.  1950 tokens over 16 experts (195-278 rows
 # each) make 576 up tiles, 8 more per XCD than its 64 blocks on MI355X,
 # so the up launch claims: with H = 1024 (16 K stages) whole leftover tiles,
