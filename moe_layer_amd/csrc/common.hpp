@@ -112,6 +112,35 @@ __device__ __forceinline__ bool last_to_arrive(int* ctr, int n, int* s_flag) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 
+// Whether the LDS-tiled kernels take every group of the launch (else none),
+// evaluated by one wave from the group sizes: the groups with more than m_min
+// rows hold at least a quarter of all rows, and all groups together make at
+// least min_tiles tiles of tile_rows token rows x n_nt weight tiles.  Under
+// skewed routing the hot groups then read each weight tile once per 128
+// rows, and the small groups ride along in the same launch instead of a
+// second one (Qwen3-235B EP share, Zipf routing, step B = 512 208 -> 158 us,
+// B = 1024 238 -> 177 us; TP share B = 1024 272 -> 201 us).  Under uniform
+// routing at B = 512 (groups of 33-64 rows, m_min = 64) no group qualifies
+// and the wave-streaming kernel's 64-row passes stay faster; from B = 1024
+// every group holds more than 32 rows.  Lane-uniform result.
+__device__ __forceinline__ bool tile_take_all(const int* __restrict__ offsets, int n_groups, int m_min,
+                                              int min_tiles, int tile_rows, int n_nt) {
+  int tiles = 0, rows = 0, hot = 0;
+  for (int g = lane_id(); g < n_groups; g += WAVE) {
+    const int m = offsets[g + 1] - offsets[g];
+    tiles += (m + tile_rows - 1) / tile_rows * n_nt;
+    rows += m;
+    if (m > m_min) hot += m;
+  }
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    tiles += __shfl_xor(tiles, d, WAVE);
+    rows += __shfl_xor(rows, d, WAVE);
+    hot += __shfl_xor(hot, d, WAVE);
+  }
+  return hot > 0 && 4LL * hot >= rows && tiles >= min_tiles;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele with shuffles).
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int l = lane_id();

@@ -107,40 +107,26 @@ __device__ __forceinline__ int tl_wrow(int tid) {
 __device__ __forceinline__ int tl_uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Wave 0: s_off[g] = offsets[g]; s_tstart[g] = tiles of the groups before g.
-// The kernel runs if the groups with more than TILE_M_MIN rows make at least
-// min_tiles tiles; it then takes the groups with more than m_min rows when
-// there are none (the wave-streaming kernel then takes every group in one
-// pass), else all groups above TILE_M_MIN.
+// The kernel takes every group or none, by tile_take_all (the wave-streaming
+// kernel evaluates the same rule and takes the rest).
 __device__ __forceinline__ void tile_prefix(const TArgs& a, int* s_tstart, int* s_off) {
   if (threadIdx.x >= WAVE) return;
   const int l = lane_id();
-  int t32 = 0, twide = 0;
-  for (int g = l; g < a.n_groups; g += WAVE) {
-    const int m = a.offsets[g + 1] - a.offsets[g];
-    const int t = (m + TL_M - 1) / TL_M * a.n_nt;
-    if (m > TILE_M_MIN) t32 += t;
-    if (m > a.m_min) twide += t;
-  }
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    t32 += __shfl_xor(t32, d, WAVE);
-    twide += __shfl_xor(twide, d, WAVE);
-  }
-  const int take = twide == 0 ? a.m_min : TILE_M_MIN;
+  const bool all = tile_take_all(a.offsets, a.n_groups, a.m_min, a.min_tiles, TL_M, a.n_nt);
   int base = 0;
   for (int g0 = 0; g0 <= a.n_groups; g0 += WAVE) {
     const int g = g0 + l;
     if (g <= a.n_groups) s_off[g] = a.offsets[g];
     int v = 0;
-    if (g < a.n_groups) {
+    if (g < a.n_groups && all) {
       const int m = a.offsets[g + 1] - a.offsets[g];
-      if (m > take) v = (m + TL_M - 1) / TL_M * a.n_nt;
+      v = (m + TL_M - 1) / TL_M * a.n_nt;
     }
     const int incl = wave_inclusive_scan(v);
     if (g < a.n_groups) s_tstart[g] = base + incl - v;
     base += __shfl(incl, WAVE - 1, WAVE);
   }
-  if (l == 0) s_tstart[a.n_groups] = t32 >= a.min_tiles ? base : 0;
+  if (l == 0) s_tstart[a.n_groups] = base;
 }
 
 __device__ __forceinline__ uint4 tl_ldg_nt(const char* base, uint32_t off) {
@@ -544,7 +530,8 @@ static int tile_resident_blocks() {
 
 // Tiles of one launch at most: groups with more than m_min rows number at
 // most pairs / (m_min + 1) (and at most n_groups), and hold at most
-// pairs / 128 + that many token tiles.
+// pairs / 128 + that many token tiles.  The kernels may take every
+// non-empty group, so the counters are sized with m_min = 0.
 static long long tile_bound(int T, int kk, int n_groups, int m_min, int n_nt) {
   const long long pairs = static_cast<long long>(T) * kk;
   long long big = pairs / (m_min + 1);
@@ -554,8 +541,8 @@ static long long tile_bound(int T, int kk, int n_groups, int m_min, int n_nt) {
 
 // Split-tile counters (one per tile at most), then the claim counters.
 static long long tl_split_ctrs(int T, int kk, int n_groups, int H, int I) {
-  long long n = tile_bound(T, kk, n_groups, TILE_M_MIN, expert_tile_nt(true, H, I));
-  const long long d = tile_bound(T, kk, n_groups, TILE_M_MIN, expert_tile_nt(false, H, I));
+  long long n = tile_bound(T, kk, n_groups, 0, expert_tile_nt(true, H, I));
+  const long long d = tile_bound(T, kk, n_groups, 0, expert_tile_nt(false, H, I));
   return d > n ? d : n;
 }
 static size_t tl_ctr_bytes(int T, int kk, int n_groups, int H, int I) {
@@ -564,12 +551,11 @@ static size_t tl_ctr_bytes(int T, int kk, int n_groups, int H, int I) {
 }
 
 // The grid is every block that fits on the chip at once (a multiple of the
-// XCD count, at most TL_MAX_GRID); the tile path runs only when the groups
-// above m_min make at least a third of a tile per compute unit (fewer tiles
-// leave most of the chip idle, and the wave-streaming kernel does better).
-// When the wave-streaming kernel takes 64-row passes (m_min is
-// TILE_M_MIN_WIDE) it reads a hot group's weights few enough times, from L2,
-// that the tile path needs a tile per compute unit to be worth its launch.
+// XCD count, at most TL_MAX_GRID); the tile path takes the groups only when
+// they make at least a third of a tile per compute unit (fewer tiles leave
+// most of the chip idle, and the wave-streaming kernel does better).  When
+// the wave-streaming kernel takes 64-row passes (m_min is TILE_M_MIN_WIDE) it
+// needs a tile per compute unit.
 static int tile_min_tiles(int m_min) {
   return m_min >= TILE_M_MIN_WIDE ? device_cu_count() : (device_cu_count() + 2) / 3;
 }

@@ -71,14 +71,15 @@ void launch_expert_down(int dtype, const void* a, const int32_t* offsets, int n_
 // LDS-tiled expert kernels (expert_tile.hip) for groups holding many rows:
 // for bf16 and T > TILE_T_MIN, launch_expert_up/down first launch them (the
 // down-projection not for W2 rows of at most 512 bytes, which the short-row
-// kernel of expert_short.hip takes whole) on
-// every group with more than m_min sorted rows (TILE_M_MIN, or
+// kernel of expert_short.hip takes whole).  They take every group of the
+// launch when the groups with more than m_min sorted rows (TILE_M_MIN, or
 // TILE_M_MIN_WIDE when the wave-streaming kernel holds four token tiles and
-// takes up to 64 rows in one pass), provided those groups
-// make at least expert_tile_min_tiles(m_min) tiles of TILE_ROWS token rows x
-// (up: 64 intermediate columns; down: 128 output features); the
-// wave-streaming kernel then skips exactly those groups.  Both kernels take
-// this decision on the device, from the same counts and the same formula.
+// takes up to 64 rows in one pass) hold at least a quarter of the rows, and
+// all groups make at least expert_tile_min_tiles(m_min) tiles of TILE_ROWS
+// token rows x (up: 64 intermediate columns; down: 128 output features);
+// otherwise none, and the wave-streaming kernel takes every group.  Both
+// kernels take this decision on the device, from the same counts and the
+// same formula (tile_take_all in common.hpp).
 constexpr int TILE_M_MIN = 32;
 constexpr int TILE_M_MIN_WIDE = 64;
 constexpr int TILE_T_MIN = 256;

@@ -58,26 +58,10 @@ __device__ __forceinline__ void item_prefix(const int* __restrict__ offsets, int
                                             int* s_ntx) {
   if (threadIdx.x >= WAVE) return;
   const int l = lane_id();
-  // The tile kernel's decision, by the same formula: it runs if the groups
-  // with more than TILE_M_MIN rows make at least tile_min tiles, and takes
-  // the groups above tile_m_min rows when there are none (every group then
-  // fits one pass here), else all groups above TILE_M_MIN.
+  // The tile kernel's decision, by the same formula: when it takes every
+  // group, none is left here.
   int m_max = 0x7fffffff;
-  if (tile_nt > 0) {
-    int t32 = 0, twide = 0;
-    for (int g = l; g < n_groups; g += WAVE) {
-      const int m = offsets[g + 1] - offsets[g];
-      const int t = (m + TILE_ROWS - 1) / TILE_ROWS * tile_nt;
-      if (m > TILE_M_MIN) t32 += t;
-      if (m > tile_m_min) twide += t;
-    }
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) {
-      t32 += __shfl_xor(t32, d, WAVE);
-      twide += __shfl_xor(twide, d, WAVE);
-    }
-    if (t32 >= tile_min) m_max = twide == 0 ? tile_m_min : TILE_M_MIN;
-  }
+  if (tile_nt > 0 && tile_take_all(offsets, n_groups, tile_m_min, tile_min, TILE_ROWS, tile_nt)) m_max = -1;
   int ntx = NT;
   if (NT == 4) {
     int big = 0;

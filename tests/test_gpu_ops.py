@@ -36,7 +36,7 @@ def test_ragged_batches(T, dtype):
 @pytest.mark.parametrize("H,E,k,I,T,n_shared,view,P", [
     (1568, 8, 2, 736, 300, 0, "full", 1),    # ragged, partial tiles and stages
     (1536, 4, 2, 768, 600, 0, "full", 1),    # ~300 rows per group: 3 token tiles
-    (1536, 16, 4, 768, 300, 2, "full", 1),   # shared groups, some routed groups streamed
+    (1536, 16, 4, 768, 300, 2, "full", 1),   # shared groups of 300 rows with the routed ones
     (2048, 16, 4, 1536, 300, 0, "tp", 2),    # TP slice: I' = 768
     (1536, 16, 4, 768, 600, 0, "ep", 2),     # EP share of 8 experts
     (1536, 4, 1, 768, 300, 0, "full", 1),    # too few tiles: all groups streamed
@@ -91,12 +91,13 @@ def test_four_token_tiles(T, E, k, hot, dtype):
     gh.check_layer(d, cfg, g)
 
 
-# A launch whose wave-streaming kernel holds four token tiles runs the
-# LDS-tiled kernels only with a tile per compute unit: 600 tokens over 8
-# experts (137-166 rows each, two token tiles) with I = 1024 and H = 2048
+# A launch whose wave-streaming kernel holds four token tiles hands its
+# groups to the LDS-tiled kernels only when those above 64 rows hold a
+# quarter of the rows and all make a tile per compute unit: 600 tokens over
+# 8 experts (137-166 rows each, two token tiles) with I = 1024 and H = 2048
 # make 256 up and 256 down tiles (one per MI355X compute unit), so the tiled
-# kernels run and take every group, and the wave-streaming launch, deciding
-# by the same device-side rule, finds nothing left.
+# kernels take every group, and the wave-streaming launch, deciding by the
+# same device-side rule, finds nothing left.
 def test_four_token_tiles_with_tiled_groups():
     import gpu_helpers as gh
     cfg = small(H=2048, E=8, k=2, I=1024, T=600)
