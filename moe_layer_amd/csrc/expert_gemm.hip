@@ -665,10 +665,15 @@ void launch_expert_up(int dtype, const void* x, const int32_t* sorted_pair, cons
   a.K = H;
   a.I_loc = I;
   a.H = H;
-  if (expert_tile_used(T, dtype))
-    launch_expert_up_tiles(x, sorted_pair, offsets, n_groups, T, kk, w13, H, I, A, expert_tile_m_min(T, kk, n_groups),
+  // From TILE_ONLY_T tokens on the LDS-tiled kernels take every group and
+  // the wave-streaming launch (which would find nothing) is not made.
+  const bool tiles = expert_tile_used(T, dtype);
+  const bool tiles_only = tiles && T >= TILE_ONLY_T;
+  if (tiles)
+    launch_expert_up_tiles(x, sorted_pair, offsets, n_groups, T, kk, w13, H, I, A,
+                           tiles_only ? -1 : expert_tile_m_min(T, kk, n_groups),
                            static_cast<char*>(ws) + stream_workspace_bytes(T, kk, n_groups, H, I, dtype), s);
-  launch_mode<XMODE_UP>(dtype, a, T, kk, ws, s);
+  if (!tiles_only) launch_mode<XMODE_UP>(dtype, a, T, kk, ws, s);
 }
 
 void launch_expert_down(int dtype, const void* A, const int32_t* offsets, int n_groups, int T,
@@ -683,10 +688,13 @@ void launch_expert_down(int dtype, const void* A, const int32_t* offsets, int n_
   a.K = I;
   a.I_loc = I;
   a.H = H;
-  if (expert_tile_used(T, dtype) && !down_short(dtype, H, I))
-    launch_expert_down_tiles(A, offsets, n_groups, T, kk, w2, H, I, y_pair, expert_tile_m_min(T, kk, n_groups),
+  const bool tiles = expert_tile_used(T, dtype) && !down_short(dtype, H, I);
+  const bool tiles_only = tiles && T >= TILE_ONLY_T;
+  if (tiles)
+    launch_expert_down_tiles(A, offsets, n_groups, T, kk, w2, H, I, y_pair,
+                             tiles_only ? -1 : expert_tile_m_min(T, kk, n_groups),
                              static_cast<char*>(ws) + stream_workspace_bytes(T, kk, n_groups, H, I, dtype), s);
-  launch_mode<XMODE_DOWN>(dtype, a, T, kk, ws, s);
+  if (!tiles_only) launch_mode<XMODE_DOWN>(dtype, a, T, kk, ws, s);
 }
 
 }  // namespace moe

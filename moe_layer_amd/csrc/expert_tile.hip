@@ -73,8 +73,8 @@ struct TArgs {
   int I_loc;
   int H;
   int n_nt;                // weight tiles per group
-  int m_min;               // groups with more rows than this are computed here ...
-  int min_tiles;           // ... when they make at least this many tiles
+  int m_min;               // hot-group row threshold of tile_take_all (-1: every group) ...
+  int min_tiles;           // ... and the tiles all groups must make
   int* ctr;                // per-tile arrival counters of split tiles (zero between calls)
   int* claim;              // the launch's claim counter, then an exit counter (zero between calls)
   float* part;             // two fp32 partial tiles per block
@@ -566,7 +566,7 @@ static void tile_launch(TArgs a, int T, void* ws, hipStream_t s) {
   if (grid > TL_MAX_GRID) grid = TL_MAX_GRID;
   grid = grid / TL_XCD * TL_XCD;
   if (grid < TL_XCD) grid = TL_XCD;
-  a.min_tiles = tile_min_tiles(a.m_min);
+  a.min_tiles = a.m_min < 0 ? 0 : tile_min_tiles(a.m_min);
   a.ctr = static_cast<int*>(ws);
   a.claim = a.ctr + tl_split_ctrs(T, a.kk, a.n_groups, a.H, a.I_loc);
   a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + tl_ctr_bytes(T, a.kk, a.n_groups, a.H, a.I_loc));
@@ -598,7 +598,7 @@ void launch_expert_up_tiles(const void* x, const int32_t* sorted_pair, const int
   a.I_loc = I;
   a.H = H;
   a.n_nt = expert_tile_nt(true, H, I);
-  a.m_min = m_min < TILE_M_MIN ? TILE_M_MIN : m_min;
+  a.m_min = m_min < 0 ? -1 : (m_min < TILE_M_MIN ? TILE_M_MIN : m_min);
   tile_launch<TMODE_UP>(a, T, ws, s);
 }
 
@@ -615,7 +615,7 @@ void launch_expert_down_tiles(const void* A, const int32_t* offsets, int n_group
   a.I_loc = I;
   a.H = H;
   a.n_nt = expert_tile_nt(false, H, I);
-  a.m_min = m_min < TILE_M_MIN ? TILE_M_MIN : m_min;
+  a.m_min = m_min < 0 ? -1 : (m_min < TILE_M_MIN ? TILE_M_MIN : m_min);
   tile_launch<TMODE_DOWN>(a, T, ws, s);
 }
 

@@ -83,6 +83,11 @@ void launch_expert_down(int dtype, const void* a, const int32_t* offsets, int n_
 constexpr int TILE_M_MIN = 32;
 constexpr int TILE_M_MIN_WIDE = 64;
 constexpr int TILE_T_MIN = 256;
+// From this many tokens on the LDS-tiled kernels take every group (m_min =
+// -1 forces tile_take_all) and no wave-streaming launch follows them: at
+// these batches the rule above already hands them every group of the
+// workloads measured here, and the streaming launch cost ~4.5 us for nothing.
+constexpr int TILE_ONLY_T = 1024;
 constexpr int TILE_ROWS = 128;
 inline int expert_tile_nt(bool up, int H, int I) { return up ? (I + 63) / 64 : (H + 127) / 128; }
 int expert_tile_min_tiles(int m_min);
