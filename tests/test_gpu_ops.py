@@ -52,6 +52,21 @@ def test_tiled_groups(H, E, k, I, T, n_shared, view, P):
     gh.check_layer(d, cfg, g)
 
 
+# From 1024 tokens on the LDS-tiled kernels take every group and no
+# wave-streaming launch follows, whatever the group sizes: 1030 tokens over
+# 128 experts with k = 2 make groups of 7-27 rows (none would qualify under
+# the hot-group rule), each in one 128-row token tile, and a ragged last
+# token tile of the batch.
+def test_small_groups_from_1024_tokens_in_tiles():
+    import gpu_helpers as gh
+    cfg = small(H=512, E=128, k=2, I=256, T=1030)
+    d = make_layer_inputs(cfg, 1030, routing="uniform", seed=43)  # no near-ties
+    print("[case] small groups in tiles T=1030 E=128 k=2 H=512 I=256", flush=True)
+    g = gh.gpu_layer(d, cfg)
+    assert g["counts"].max() <= 32, g["counts"]
+    gh.check_layer(d, cfg, g)
+
+
 # A single hot expert holding every token: one group far above the 32-row
 # line, too few tiles for the tiled kernels, so the wave-streaming kernel
 # takes it in passes of 32 rows.
